@@ -1,0 +1,98 @@
+"""ctypes view of libexattn.so: the problem struct and the C entry points.
+
+The declarations mirror ``include/exattn.h``. Loading fails loudly when the library has
+not been built: there is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libexattn.so")
+
+ABI_VERSION = 1
+
+OK = 0
+STATUS_NAMES = {
+    0: "EXATTN_OK", 1: "EXATTN_ERR_NULL", 2: "EXATTN_ERR_DTYPE", 3: "EXATTN_ERR_HEAD_DIM",
+    4: "EXATTN_ERR_SHAPE", 5: "EXATTN_ERR_STRIDE", 6: "EXATTN_ERR_ALIGN", 7: "EXATTN_ERR_MASK",
+    8: "EXATTN_ERR_VARLEN", 9: "EXATTN_ERR_WORKSPACE", 10: "EXATTN_ERR_SCALE", 11: "EXATTN_ERR_HIP",
+}
+ERR_HIP = 11
+
+DTYPE_BF16, DTYPE_FP16 = 0, 1
+MASK_NONE, MASK_BOOL_U8, MASK_ADD_BF16 = 0, 1, 2
+
+EXPORTED = (
+    "exattn_abi_version", "exattn_check", "exattn_fwd", "exattn_bwd_workspace_size",
+    "exattn_bwd", "exattn_status_string", "exattn_last_error", "exattn_timing_enable",
+    "exattn_timing_read",
+)
+
+_i32, _i64, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+
+
+class Problem(ctypes.Structure):
+    """Mirror of ``exattn_problem``."""
+    _fields_ = [
+        ("dtype", _i32), ("batch", _i32), ("seqlen_q", _i32), ("seqlen_k", _i32),
+        ("heads_q", _i32), ("heads_kv", _i32), ("head_dim", _i32), ("causal", _i32),
+        ("scale", _f32), ("mask_kind", _i32),
+        ("q_stride", _i64 * 3), ("k_stride", _i64 * 3), ("v_stride", _i64 * 3),
+        ("o_stride", _i64 * 3), ("do_stride", _i64 * 3), ("mask_stride", _i64 * 4),
+        ("mask", _vp), ("cu_seqlens_q", _vp), ("cu_seqlens_k", _vp),
+        ("num_seqs", _i32), ("max_seqlen_q", _i32), ("max_seqlen_k", _i32), ("reserved", _i32),
+    ]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load():
+    """Load libexattn.so (once) and declare its signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m exact_attention_40_amd.build` "
+                "(there is no fallback path)")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(Problem)
+        lib.exattn_abi_version.restype = ctypes.c_int
+        lib.exattn_abi_version.argtypes = []
+        lib.exattn_check.restype = ctypes.c_int
+        lib.exattn_check.argtypes = [P]
+        lib.exattn_fwd.restype = ctypes.c_int
+        lib.exattn_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp]
+        lib.exattn_bwd_workspace_size.restype = ctypes.c_size_t
+        lib.exattn_bwd_workspace_size.argtypes = [P]
+        lib.exattn_bwd.restype = ctypes.c_int
+        lib.exattn_bwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   ctypes.c_size_t, _vp]
+        lib.exattn_status_string.restype = ctypes.c_char_p
+        lib.exattn_status_string.argtypes = [ctypes.c_int]
+        lib.exattn_last_error.restype = ctypes.c_char_p
+        lib.exattn_last_error.argtypes = []
+        lib.exattn_timing_enable.restype = ctypes.c_int
+        lib.exattn_timing_enable.argtypes = [ctypes.c_int]
+        lib.exattn_timing_read.restype = ctypes.c_int
+        lib.exattn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_char_p),
+                                           ctypes.POINTER(ctypes.c_double),
+                                           ctypes.POINTER(ctypes.c_int), ctypes.c_int]
+        v = lib.exattn_abi_version()
+        if v != ABI_VERSION:
+            raise RuntimeError(f"libexattn ABI version {v}, binding expects {ABI_VERSION}")
+        _lib = lib
+        return lib
+
+
+def status_message(lib, status: int) -> str:
+    detail = lib.exattn_last_error().decode()
+    name = STATUS_NAMES.get(status, str(status))
+    return f"{name} ({lib.exattn_status_string(status).decode()}): {detail}"

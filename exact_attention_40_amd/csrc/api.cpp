@@ -1,0 +1,439 @@
+// Host side of libexattn: argument validation, grid sizing and kernel launches.
+// Every check runs before the first enqueue; on error nothing is enqueued.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/exattn.h"
+#include "params.hpp"
+
+namespace exattn {
+
+const char* kernel_name(KernelId id) {
+  switch (id) {
+    case KernelId::Fwd: return "exattn_fwd_kernel";
+    case KernelId::FwdTail: return "exattn_fwd_tail_kernel";
+    case KernelId::Delta: return "exattn_bwd_delta_kernel";
+    case KernelId::Bwd: return "exattn_bwd_kernel";
+    case KernelId::DqReduce: return "exattn_bwd_dq_reduce_kernel";
+    case KernelId::KvTail: return "exattn_bwd_kv_tail_kernel";
+    case KernelId::Zero: return "exattn_zero_kernel";
+    default: return "unknown";
+  }
+}
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+exattn_status fail(exattn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+// ---- kernel timing (HIP events around each launch) ------------------------------------
+struct TimedLaunch {
+  int kernel;
+  hipEvent_t start, stop;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<hipEvent_t> g_event_pool;
+std::vector<TimedLaunch> g_launches;
+constexpr size_t kMaxTimed = 4096;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct Timer {
+  bool on = false;
+  TimedLaunch t{};
+  Timer(KernelId id, hipStream_t s) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (!g_timing || g_launches.size() >= kMaxTimed) return;
+    t.kernel = (int)id;
+    t.start = take_event();
+    t.stop = take_event();
+    if (!t.start || !t.stop) return;
+    on = hipEventRecord(t.start, s) == hipSuccess;
+  }
+  void done(hipStream_t s) {
+    if (!on) return;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (hipEventRecord(t.stop, s) == hipSuccess) g_launches.push_back(t);
+  }
+};
+
+template <class F>
+hipError_t timed(KernelId id, hipStream_t s, F&& f) {
+  Timer tm(id, s);
+  hipError_t e = f();
+  tm.done(s);
+  return e;
+}
+
+// ---- validation --------------------------------------------------------------------------
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+exattn_status check_strides(const int64_t* st, bool varlen, const char* name) {
+  for (int i = varlen ? 1 : 0; i < 3; ++i) {
+    if (st[i] < 0 || (st[i] & 7) != 0)
+      return fail(EXATTN_ERR_STRIDE, "%s stride[%d] = %lld must be a non-negative multiple of 8",
+                  name, i, (long long)st[i]);
+  }
+  return EXATTN_OK;
+}
+
+exattn_status validate(const exattn_problem* p, bool bwd) {
+  if (!p) return fail(EXATTN_ERR_NULL, "problem pointer is NULL");
+  if (p->dtype != EXATTN_DTYPE_BF16)
+    return fail(EXATTN_ERR_DTYPE, "dtype %d is not supported: only bf16 (0) is accepted", p->dtype);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(EXATTN_ERR_HEAD_DIM, "head_dim %d is not supported: only 64 and 128", p->head_dim);
+  if (p->heads_q < 1 || p->heads_kv < 1 || p->heads_q % p->heads_kv != 0)
+    return fail(EXATTN_ERR_SHAPE, "heads_q=%d must be a positive multiple of heads_kv=%d",
+                p->heads_q, p->heads_kv);
+  if (p->seqlen_q < 0 || p->seqlen_k < 0)
+    return fail(EXATTN_ERR_SHAPE, "negative sequence length");
+  if (p->causal != 0 && p->causal != 1) return fail(EXATTN_ERR_SHAPE, "causal must be 0 or 1");
+  if (!std::isfinite(p->scale)) return fail(EXATTN_ERR_SCALE, "scale must be finite");
+  const bool varlen = p->cu_seqlens_q != nullptr || p->cu_seqlens_k != nullptr;
+  if (varlen) {
+    if (!p->cu_seqlens_q || !p->cu_seqlens_k)
+      return fail(EXATTN_ERR_VARLEN, "cu_seqlens_q and cu_seqlens_k must both be given");
+    if (p->num_seqs < 1) return fail(EXATTN_ERR_VARLEN, "num_seqs must be >= 1");
+    if (p->max_seqlen_q < 0 || p->max_seqlen_k < 0)
+      return fail(EXATTN_ERR_VARLEN, "max_seqlen must be >= 0");
+    if (p->max_seqlen_q > p->seqlen_q || p->max_seqlen_k > p->seqlen_k)
+      return fail(EXATTN_ERR_VARLEN, "max_seqlen exceeds the packed row count");
+    if (p->mask_kind != EXATTN_MASK_NONE)
+      return fail(EXATTN_ERR_MASK, "a mask cannot be combined with cu_seqlens");
+  } else {
+    if (p->batch < 0) return fail(EXATTN_ERR_SHAPE, "negative batch");
+  }
+  if (p->mask_kind < EXATTN_MASK_NONE || p->mask_kind > EXATTN_MASK_ADD_BF16)
+    return fail(EXATTN_ERR_MASK, "unknown mask kind %d", p->mask_kind);
+  if (p->mask_kind != EXATTN_MASK_NONE) {
+    if (!p->mask) return fail(EXATTN_ERR_MASK, "mask pointer is NULL");
+    for (int i = 0; i < 3; ++i)
+      if (p->mask_stride[i] < 0) return fail(EXATTN_ERR_MASK, "negative mask stride");
+    if (p->mask_stride[3] != 1) return fail(EXATTN_ERR_MASK, "mask key stride must be 1");
+    if (p->mask_kind == EXATTN_MASK_ADD_BF16 && (reinterpret_cast<uintptr_t>(p->mask) & 1u))
+      return fail(EXATTN_ERR_ALIGN, "bf16 mask pointer must be 2-byte aligned");
+  }
+  exattn_status s;
+  if ((s = check_strides(p->q_stride, varlen, "q")) != EXATTN_OK) return s;
+  if ((s = check_strides(p->k_stride, varlen, "k")) != EXATTN_OK) return s;
+  if ((s = check_strides(p->v_stride, varlen, "v")) != EXATTN_OK) return s;
+  if (bwd) {
+    if ((s = check_strides(p->o_stride, varlen, "out")) != EXATTN_OK) return s;
+    if ((s = check_strides(p->do_stride, varlen, "dout")) != EXATTN_OK) return s;
+  }
+  // Size limits: row counts times heads must index within int32 rows, blocks within 2^31.
+  const int64_t rows_q = varlen ? (int64_t)p->seqlen_q : (int64_t)p->batch * p->seqlen_q;
+  const int64_t rows_k = varlen ? (int64_t)p->seqlen_k : (int64_t)p->batch * p->seqlen_k;
+  if (rows_q > INT32_MAX || rows_k > INT32_MAX || rows_q * p->heads_q > INT32_MAX ||
+      rows_k * p->heads_kv > INT32_MAX)
+    return fail(EXATTN_ERR_SHAPE, "problem too large");
+  return EXATTN_OK;
+}
+
+struct Geometry {
+  bool varlen;
+  int units;
+  int64_t rows_q, rows_k;
+};
+
+Geometry geometry(const exattn_problem* p) {
+  Geometry g;
+  g.varlen = p->cu_seqlens_q != nullptr;
+  g.units = g.varlen ? p->num_seqs : p->batch;
+  g.rows_q = g.varlen ? p->seqlen_q : (int64_t)p->batch * p->seqlen_q;
+  g.rows_k = g.varlen ? p->seqlen_k : (int64_t)p->batch * p->seqlen_k;
+  return g;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WsLayout {
+  size_t dq_acc, lse2, delta, total;
+};
+
+WsLayout ws_layout(const exattn_problem* p) {
+  const Geometry g = geometry(p);
+  WsLayout w;
+  const size_t nq = (size_t)g.rows_q * p->heads_q;
+  w.dq_acc = 0;
+  w.lse2 = align256(nq * p->head_dim * sizeof(float));
+  w.delta = w.lse2 + align256(nq * sizeof(float));
+  w.total = w.delta + align256(nq * sizeof(float));
+  return w;
+}
+
+void fill_common(const exattn_problem* p, int64_t* qs, int64_t* ks, int64_t* vs) {
+  for (int i = 0; i < 3; ++i) {
+    qs[i] = p->q_stride[i];
+    ks[i] = p->k_stride[i];
+    vs[i] = p->v_stride[i];
+  }
+}
+
+exattn_status hip_fail(hipError_t e, const char* what) {
+  return fail(EXATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+}  // namespace exattn
+
+using namespace exattn;
+
+extern "C" {
+
+int exattn_abi_version(void) { return EXATTN_ABI_VERSION; }
+
+exattn_status exattn_check(const exattn_problem* p) {
+  g_err[0] = 0;
+  return validate(p, false);
+}
+
+const char* exattn_status_string(exattn_status s) {
+  switch (s) {
+    case EXATTN_OK: return "ok";
+    case EXATTN_ERR_NULL: return "null pointer";
+    case EXATTN_ERR_DTYPE: return "unsupported dtype";
+    case EXATTN_ERR_HEAD_DIM: return "unsupported head_dim";
+    case EXATTN_ERR_SHAPE: return "invalid shape";
+    case EXATTN_ERR_STRIDE: return "invalid stride";
+    case EXATTN_ERR_ALIGN: return "misaligned pointer";
+    case EXATTN_ERR_MASK: return "invalid mask";
+    case EXATTN_ERR_VARLEN: return "invalid packed-sequence description";
+    case EXATTN_ERR_WORKSPACE: return "invalid workspace";
+    case EXATTN_ERR_SCALE: return "non-finite scale";
+    case EXATTN_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* exattn_last_error(void) { return g_err; }
+
+exattn_status exattn_fwd(const exattn_problem* p, const void* q, const void* k, const void* v,
+                         void* out, float* lse, void* stream) {
+  g_err[0] = 0;
+  exattn_status st = validate(p, false);
+  if (st != EXATTN_OK) return st;
+  const Geometry g = geometry(p);
+  const bool any = g.rows_q > 0 && p->heads_q > 0;
+  if (any && (!q || !out || !lse)) return fail(EXATTN_ERR_NULL, "q, out or lse is NULL");
+  if (any && g.rows_k > 0 && (!k || !v)) return fail(EXATTN_ERR_NULL, "k or v is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(EXATTN_ERR_ALIGN, "q/k/v/out must be 16-byte aligned and lse 4-byte aligned");
+  if (!any) return EXATTN_OK;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int D = p->head_dim, H = p->heads_q;
+  FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.q_sb = p->q_stride[0]; a.q_ss = p->q_stride[1]; a.q_sh = p->q_stride[2];
+  a.k_sb = p->k_stride[0]; a.k_ss = p->k_stride[1]; a.k_sh = p->k_stride[2];
+  a.v_sb = p->v_stride[0]; a.v_ss = p->v_stride[1]; a.v_sh = p->v_stride[2];
+  // out is written contiguous
+  a.o_sh = D;
+  a.o_ss = (int64_t)H * D;
+  a.o_sb = (int64_t)p->seqlen_q * H * D;
+  a.mask = p->mask;
+  a.m_sb = p->mask_stride[0];
+  a.m_sh = p->mask_stride[1];
+  a.m_si = p->mask_stride[2];
+  a.cu_q = p->cu_seqlens_q;
+  a.cu_k = p->cu_seqlens_k;
+  a.B = g.varlen ? 1 : p->batch;
+  a.Sq = p->seqlen_q;
+  a.Sk = p->seqlen_k;
+  a.H = H;
+  a.Hkv = p->heads_kv;
+  a.group = H / p->heads_kv;
+  a.num_units = g.units;
+  const int bm = fwd_block_m(D);
+  const int maxq = g.varlen ? p->max_seqlen_q : p->seqlen_q;
+  a.num_q_tiles = (maxq + bm - 1) / bm;
+  a.lse_row = p->seqlen_q;
+  a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
+  if ((int64_t)a.num_units * H * a.num_q_tiles > INT32_MAX)
+    return fail(EXATTN_ERR_SHAPE, "too many query tiles");
+
+  hipError_t e;
+  if (a.num_q_tiles > 0) {
+    e = timed(KernelId::Fwd, s, [&] {
+      return launch_fwd(a, D, p->causal != 0, p->mask_kind, g.varlen, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
+  }
+  if (g.varlen) {
+    e = timed(KernelId::FwdTail, s, [&] { return launch_fwd_tail(a, D, s); });
+    if (e != hipSuccess) return hip_fail(e, "forward tail launch");
+  }
+  return EXATTN_OK;
+}
+
+size_t exattn_bwd_workspace_size(const exattn_problem* p) {
+  if (validate(p, true) != EXATTN_OK) return 0;
+  return ws_layout(p).total;
+}
+
+exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, const void* v,
+                         const void* out, const void* dout, const float* lse, void* dq,
+                         void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  g_err[0] = 0;
+  exattn_status st = validate(p, true);
+  if (st != EXATTN_OK) return st;
+  const Geometry g = geometry(p);
+  const bool anyq = g.rows_q > 0;
+  const bool anyk = g.rows_k > 0;
+  if (anyq && (!q || !out || !dout || !lse || !dq))
+    return fail(EXATTN_ERR_NULL, "q, out, dout, lse or dq is NULL");
+  if (anyk && (!k || !v || !dk || !dv)) return fail(EXATTN_ERR_NULL, "k, v, dk or dv is NULL");
+  const void* ptrs[] = {q, k, v, out, dout, dq, dk, dv};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return fail(EXATTN_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(EXATTN_ERR_ALIGN, "lse must be 4-byte aligned");
+  const WsLayout w = ws_layout(p);
+  if (anyq) {  // the workspace is only touched when there are query rows
+    if (!workspace) return fail(EXATTN_ERR_WORKSPACE, "workspace is NULL");
+    if (workspace_bytes < w.total)
+      return fail(EXATTN_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, w.total);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(EXATTN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  if (!anyq && !anyk) return EXATTN_OK;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int D = p->head_dim, H = p->heads_q;
+  unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
+  BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dq_acc = reinterpret_cast<float*>(ws + w.dq_acc);
+  a.lse2 = reinterpret_cast<float*>(ws + w.lse2);
+  a.delta = reinterpret_cast<float*>(ws + w.delta);
+  a.q_sb = p->q_stride[0]; a.q_ss = p->q_stride[1]; a.q_sh = p->q_stride[2];
+  a.k_sb = p->k_stride[0]; a.k_ss = p->k_stride[1]; a.k_sh = p->k_stride[2];
+  a.v_sb = p->v_stride[0]; a.v_ss = p->v_stride[1]; a.v_sh = p->v_stride[2];
+  a.o_sb = p->o_stride[0]; a.o_ss = p->o_stride[1]; a.o_sh = p->o_stride[2];
+  a.do_sb = p->do_stride[0]; a.do_ss = p->do_stride[1]; a.do_sh = p->do_stride[2];
+  a.mask = p->mask;
+  a.m_sb = p->mask_stride[0];
+  a.m_sh = p->mask_stride[1];
+  a.m_si = p->mask_stride[2];
+  a.cu_q = p->cu_seqlens_q;
+  a.cu_k = p->cu_seqlens_k;
+  a.B = g.varlen ? 1 : p->batch;
+  a.Sq = p->seqlen_q;
+  a.Sk = p->seqlen_k;
+  a.H = H;
+  a.Hkv = p->heads_kv;
+  a.group = H / p->heads_kv;
+  a.num_units = g.units;
+  const int bn = bwd_block_n(D);
+  const int maxk = g.varlen ? p->max_seqlen_k : p->seqlen_k;
+  a.num_k_blocks = (maxk + bn - 1) / bn;
+  a.lse_row = p->seqlen_q;
+  a.rows_q = (int)g.rows_q;
+  a.rows_k = (int)g.rows_k;
+  a.scale = p->scale;
+  a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
+  if ((int64_t)a.num_units * a.Hkv * a.num_k_blocks > INT32_MAX)
+    return fail(EXATTN_ERR_SHAPE, "too many key blocks");
+
+  hipError_t e;
+  if (!anyq) {
+    // no query rows: every key receives zero gradient
+    const int64_t bytes = g.rows_k * p->heads_kv * D * 2;
+    e = timed(KernelId::Zero, s, [&] { return launch_zero16(dk, bytes, s); });
+    if (e == hipSuccess) e = timed(KernelId::Zero, s, [&] { return launch_zero16(dv, bytes, s); });
+    if (e != hipSuccess) return hip_fail(e, "zero dk/dv");
+    return EXATTN_OK;
+  }
+  e = timed(KernelId::Delta, s, [&] { return launch_delta(a, D, g.varlen, s); });
+  if (e != hipSuccess) return hip_fail(e, "delta kernel launch");
+  if (a.num_k_blocks > 0) {
+    e = timed(KernelId::Bwd, s, [&] {
+      return launch_bwd(a, D, p->causal != 0, p->mask_kind, g.varlen, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
+  }
+  e = timed(KernelId::DqReduce, s, [&] { return launch_dq_reduce(a, D, s); });
+  if (e != hipSuccess) return hip_fail(e, "dq reduce launch");
+  if (g.varlen && anyk) {
+    e = timed(KernelId::KvTail, s, [&] { return launch_kv_tail(a, D, s); });
+    if (e != hipSuccess) return hip_fail(e, "kv tail launch");
+  }
+  return EXATTN_OK;
+}
+
+exattn_status exattn_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = enable != 0;
+  return EXATTN_OK;
+}
+
+int exattn_timing_read(const char** names, double* total_ms, int* launches, int max) {
+  std::vector<TimedLaunch> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    recs.swap(g_launches);
+  }
+  const int nk = (int)KernelId::Count;
+  std::vector<double> ms(nk, 0.0);
+  std::vector<int> cnt(nk, 0);
+  int rc = 0;
+  for (auto& r : recs) {
+    if (hipEventSynchronize(r.stop) != hipSuccess) rc = -1;
+    float t = 0.f;
+    if (rc == 0 && hipEventElapsedTime(&t, r.start, r.stop) == hipSuccess) {
+      ms[r.kernel] += t;
+      cnt[r.kernel] += 1;
+    }
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    for (auto& r : recs) {
+      g_event_pool.push_back(r.start);
+      g_event_pool.push_back(r.stop);
+    }
+  }
+  if (rc != 0) return -1;
+  int n = 0;
+  for (int i = 0; i < nk && n < max; ++i) {
+    if (cnt[i] == 0) continue;
+    if (names) names[n] = kernel_name((KernelId)i);
+    if (total_ms) total_ms[n] = ms[i];
+    if (launches) launches[n] = cnt[i];
+    ++n;
+  }
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Kernel argument blocks and launcher declarations (host and device).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace exattn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  const void* mask;
+  int64_t m_sb, m_sh, m_si;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int B, Sq, Sk, H, Hkv, group;
+  int num_units;     // batch (dense) or num_seqs (packed)
+  int num_q_tiles;   // per unit
+  int lse_row;       // packed: row count of lse ([H, lse_row]); dense: Sq
+  float scale_log2;  // scale * log2(e)
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dq_acc;     // fp32 [rows_q, H, D]
+  float* lse2;       // fp32, lse layout: lse * log2(e), +inf for empty rows
+  float* delta;      // fp32, lse layout: rowsum(dout * out)
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t do_sb, do_ss, do_sh;
+  const void* mask;
+  int64_t m_sb, m_sh, m_si;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int B, Sq, Sk, H, Hkv, group;
+  int num_units;
+  int num_k_blocks;  // per (unit, kv head)
+  int lse_row;
+  int rows_q;        // rows of q per head in total: B*Sq (dense) or total_q (packed)
+  int rows_k;
+  float scale;
+  float scale_log2;
+};
+
+enum class KernelId : int { Fwd = 0, FwdTail, Delta, Bwd, DqReduce, KvTail, Zero, Count };
+
+const char* kernel_name(KernelId id);
+
+// Launchers return hipGetLastError() after the launch. `variant` selects the tiling.
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool causal, int mask_mode, bool varlen,
+                      hipStream_t s);
+hipError_t launch_fwd_tail(const FwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_delta(const BwdArgs& a, int head_dim, bool varlen, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool causal, int mask_mode, bool varlen,
+                      hipStream_t s);
+hipError_t launch_dq_reduce(const BwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_kv_tail(const BwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_zero16(void* p, int64_t bytes, hipStream_t s);  // bytes % 16 == 0
+
+// Tile shapes the host needs for grid sizing.
+int fwd_block_m(int head_dim);
+int bwd_block_n(int head_dim);
+
+}  // namespace exattn

@@ -1,0 +1,182 @@
+/*
+ * exattn - tiled exact softmax attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of the shared library libexattn.so. Plain pointers and sizes only.
+ *
+ * The operation (forward): for every batch entry (or packed sequence) b, query head h and
+ * query row i, with g = h / (heads_q / heads_kv) the KV head of h:
+ *   s_ij  = scale * q_i . k_j  (+ a_ij for an additive mask)
+ *   key j is hidden when j >= the sequence's key count, when causal and j > i
+ *   (top-left alignment), when a bool mask holds 0, or when an additive mask holds -inf;
+ *   out_i = sum_j softmax_j(s_ij) v_j over visible keys,
+ *   lse_i = ln sum_j exp(s_ij) over visible keys (natural log, fp32).
+ * A row with no visible key gets out = 0 and lse = -inf.
+ * Sources: the forward keeps a running row max and row sum and emits a log-sum-exp
+ * (FlyDSL PR #1033 "[Bugfix][Kernel] Fix NaN from the lazy rescale on a wide score range",
+ * sections "Root cause", "The fix"); masks hide keys as in OpenWAM PR #64 (cuDNN SDPA
+ * backward padding fix), section "Fix"; grouped KV heads and causal masking as in
+ * flash-dmattn PR #122 "Fix NaN/Inf values in dV gradients during backward pass",
+ * section "Problem".
+ *
+ * The operation (backward), given dout = dL/dout: P is recomputed from the stored lse as
+ * exp(s - lse) (OpenWAM PR #64, "Summary"); dv = P^T dout and dk = scale * dS^T q
+ * (flash-dmattn PR #122, "Solution", item 2), with dS = P * (dout v^T - rowsum(dout * out))
+ * and dq = scale * dS k. dk and dv of a KV head sum over the query heads that share it.
+ * Keys that no query can see receive exactly zero dk and dv.
+ *
+ * Ownership and ordering (NVIDIA cudnn-frontend PR #429 "Fix stream-ordering and
+ * input-validation holes in the SM100 DSA backward interface", first commit message):
+ *   - The caller owns every buffer. The library allocates no device memory and never
+ *     synchronises; all work is enqueued in order on the caller's `stream`
+ *     (a hipStream_t passed as void*, NULL = the null stream).
+ *   - Outputs are write-only: out, lse, dq, dk, dv are fully written, including rows of
+ *     packed tensors past cu_seqlens[num_seqs] (PFCCLab cudnn-frontend PR #9 "DSA: fix dK
+ *     SMEM handoff race and two latent NaN sources in the dense indexer", item 2), so no
+ *     result depends on their previous contents (flash-dmattn PR #122, "Root Cause" 1).
+ *   - The backward workspace is cleared by the library on `stream` before use.
+ *
+ * Errors: every argument is validated on the host before anything is enqueued. On a
+ * non-OK status nothing was enqueued and no output was touched, except EXATTN_ERR_HIP,
+ * which reports a failed kernel launch. exattn_last_error() gives a per-thread message.
+ * Rejected instead of run (cudnn-frontend PR #429, second and third commit messages;
+ * cudnn-frontend PR #9, item 4): a dtype other than bf16, a head_dim other than 64 or 128,
+ * heads_q not a multiple of heads_kv, unaligned pointers or strides, a mask together with
+ * cu_seqlens, a non-finite scale.
+ */
+#ifndef EXATTN_H
+#define EXATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EXATTN_ABI_VERSION 1
+
+typedef enum exattn_status {
+  EXATTN_OK = 0,
+  EXATTN_ERR_NULL = 1,       /* a required pointer is NULL */
+  EXATTN_ERR_DTYPE = 2,      /* dtype is not EXATTN_DTYPE_BF16 */
+  EXATTN_ERR_HEAD_DIM = 3,   /* head_dim not in {64, 128} */
+  EXATTN_ERR_SHAPE = 4,      /* negative sizes, heads_q % heads_kv != 0, size overflow */
+  EXATTN_ERR_STRIDE = 5,     /* a stride is negative or not a multiple of 8 elements */
+  EXATTN_ERR_ALIGN = 6,      /* a q/k/v/out/dout/dq/dk/dv pointer is not 16-byte aligned */
+  EXATTN_ERR_MASK = 7,       /* bad mask kind, NULL mask, negative mask stride, mask + varlen */
+  EXATTN_ERR_VARLEN = 8,     /* num_seqs < 1, max_seqlen < 0, or one cu_seqlens pointer NULL */
+  EXATTN_ERR_WORKSPACE = 9,  /* workspace NULL, too small or not 256-byte aligned */
+  EXATTN_ERR_SCALE = 10,     /* scale is NaN or infinite */
+  EXATTN_ERR_HIP = 11        /* a HIP launch failed; see exattn_last_error() */
+} exattn_status;
+
+typedef enum exattn_dtype { EXATTN_DTYPE_BF16 = 0, EXATTN_DTYPE_FP16 = 1 } exattn_dtype;
+
+typedef enum exattn_mask_kind {
+  EXATTN_MASK_NONE = 0,
+  EXATTN_MASK_BOOL_U8 = 1,   /* uint8, nonzero = attend, 0 = hidden */
+  EXATTN_MASK_ADD_BF16 = 2   /* bf16 added to the scaled score; -inf hides */
+} exattn_mask_kind;
+
+/*
+ * Problem description (host memory; read during the call only).
+ *
+ * Dense layout (cu_seqlens_q == NULL): q, dout, out are [batch, seqlen_q, heads_q, head_dim]
+ * and k, v are [batch, seqlen_k, heads_kv, head_dim], addressed through element strides
+ * x_stride = {batch, token, head}; the head_dim stride is 1. lse is a contiguous fp32
+ * [batch, heads_q, seqlen_q] array.
+ *
+ * Packed layout (cu_seqlens_q != NULL): q/dout/out are [seqlen_q, heads_q, head_dim] and k/v
+ * are [seqlen_k, heads_kv, head_dim] where seqlen_q/seqlen_k are the packed row counts
+ * (total_q, total_k); x_stride[0] is ignored. Sequence s owns query rows
+ * [cu_seqlens_q[s], cu_seqlens_q[s+1]) and key rows [cu_seqlens_k[s], cu_seqlens_k[s+1]);
+ * both arrays are int32 device memory with num_seqs + 1 non-decreasing entries starting at
+ * 0 and ending at most at seqlen_q / seqlen_k; max_seqlen_q/k bound every sequence length.
+ * lse is a contiguous fp32 [heads_q, seqlen_q] array. Causal alignment is per sequence.
+ *
+ * Gradient outputs dq, dk, dv are contiguous in the layout of q, k, v above.
+ *
+ * The mask (dense only) is indexed by element strides mask_stride = {b, h, i, j}; a stride
+ * of 0 broadcasts that axis (key-broadcast and per-batch masks); mask_stride[3] must be 1.
+ */
+typedef struct exattn_problem {
+  int32_t dtype;         /* exattn_dtype; only EXATTN_DTYPE_BF16 is accepted */
+  int32_t batch;         /* dense: batch size; packed: ignored */
+  int32_t seqlen_q;      /* dense: query length; packed: total query rows */
+  int32_t seqlen_k;      /* dense: key length; packed: total key rows */
+  int32_t heads_q;
+  int32_t heads_kv;
+  int32_t head_dim;      /* 64 or 128 */
+  int32_t causal;        /* 0 or 1 */
+  float scale;           /* multiplies q.k; finite (0 gives uniform attention) */
+  int32_t mask_kind;     /* exattn_mask_kind */
+  int64_t q_stride[3];
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];   /* out as read by the backward; the forward writes it contiguous */
+  int64_t do_stride[3];  /* dout (backward only) */
+  int64_t mask_stride[4];
+  const void* mask;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int32_t num_seqs;
+  int32_t max_seqlen_q;
+  int32_t max_seqlen_k;
+  int32_t reserved;
+} exattn_problem;
+
+/* ABI version of the loaded library (EXATTN_ABI_VERSION at build time). */
+int exattn_abi_version(void);
+
+/* Metadata-only support check: validates the description without touching device
+ * memory (cudnn-frontend PR #429: a support gate must reject what the kernels cannot
+ * run). Pointers to tensors are not checked here. */
+exattn_status exattn_check(const exattn_problem* p);
+
+/*
+ * Forward. q, k, v: bf16 device pointers laid out as described above. out: bf16 device
+ * pointer, written contiguous ([batch, seqlen_q, heads_q, head_dim] or packed
+ * [seqlen_q, heads_q, head_dim]); its o_stride entry is ignored. lse: fp32 device pointer
+ * (layout above). Every element of out and lse is written.
+ */
+exattn_status exattn_fwd(const exattn_problem* p, const void* q, const void* k,
+                         const void* v, void* out, float* lse, void* stream);
+
+/* Bytes of device workspace exattn_bwd needs for this problem (0 on invalid input). */
+size_t exattn_bwd_workspace_size(const exattn_problem* p);
+
+/*
+ * Backward. q, k, v, out, dout: bf16 device inputs (strides in p); lse: fp32 device input
+ * as written by exattn_fwd for the same problem (read only). dq, dk, dv: bf16 device
+ * outputs, contiguous, every element written. workspace: device memory of at least
+ * exattn_bwd_workspace_size(p) bytes, 256-byte aligned, owned by the caller; its contents
+ * on entry do not matter and on exit are unspecified. Concurrent calls must not share a
+ * workspace. dq accumulates fp32 partial products with atomics, so it may differ between
+ * runs by re-association of fp32 sums; out, lse, dk and dv are bitwise reproducible.
+ */
+exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, const void* v,
+                         const void* out, const void* dout, const float* lse, void* dq,
+                         void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Static description of a status code. */
+const char* exattn_status_string(exattn_status s);
+
+/* Message of the last non-OK status returned on the calling thread ("" if none). */
+const char* exattn_last_error(void);
+
+/*
+ * Kernel timing. While enabled, every kernel the library launches is bracketed by a pair
+ * of HIP events recorded on the launch stream (at most 4096 pairs between reads).
+ * exattn_timing_read waits for the recorded events, writes for up to `max` kernel names
+ * the summed milliseconds and launch counts, clears the record and returns the number of
+ * names written (or -1 on a HIP error). names[i] points to static strings.
+ */
+exattn_status exattn_timing_enable(int enable);
+int exattn_timing_read(const char** names, double* total_ms, int* launches, int max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXATTN_H */

@@ -289,22 +289,26 @@ def rows_backward_dq(q_rows, k, v, dout_rows, row_index, scale, causal,
     return dq
 
 
-def keys_backward(q, k, v, dout, key_index, scale, causal, row_chunk=1024):
+def keys_backward(q, k, v, dout, key_index, scale, causal, row_chunk=1024, row_offset=0):
     """dk and dv of selected keys of one unit, summing over every query row.
 
-    q/dout [sq, d] hold all query rows of the unit; each query row's P is the definition
-    over all keys (its normaliser needs them all), and only the selected key columns of
-    dS and P enter dk = scale * dS^T q and dv = P^T dO. Rows are visited in chunks to
-    bound memory; every row is visited exactly once.
+    q/dout [n, d] hold the unit's query rows starting at sequence-local row ``row_offset``;
+    each query row's P is the definition over all keys (its normaliser needs them all), and
+    only the selected key columns of dS and P enter dk = scale * dS^T q and dv = P^T dO.
+    Rows are visited in chunks to bound memory; every given row is visited exactly once.
+    Leaving out the rows before ``row_offset`` is exact only when none of them can see a
+    selected key, i.e. causal masking with every selected key at or after ``row_offset``.
     """
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     key_index = np.asarray(key_index)
+    if row_offset:
+        assert causal and key_index.min() >= row_offset, "rows before row_offset see the keys"
     sq = q.shape[0]
     dk = np.zeros((len(key_index), q.shape[1]))
     dv = np.zeros_like(dk)
     for r0 in range(0, sq, row_chunk):
         rows = np.arange(r0, min(sq, r0 + row_chunk))
-        vis = visibility(len(rows), k.shape[0], causal, row_index=rows)
+        vis = visibility(len(rows), k.shape[0], causal, row_index=rows + row_offset)
         out, _, P = unit_forward(q[rows], k, v, scale, vis)
         dP = dout[rows] @ v[key_index].T
         delta = np.sum(dout[rows] * out, axis=1)

@@ -1,0 +1,161 @@
+"""C-ABI tests that need no GPU: the library loads, exports every declared symbol, its
+struct layout matches the binding, and every rejection path returns a status before any
+HIP call is made (so these run on a machine without a GPU)."""
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from exact_attention_40_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "exattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(exattn_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (exattn_\w+)", out))
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert lib.exattn_abi_version() == _lib.ABI_VERSION
+
+
+def test_struct_layout_matches_header():
+    """Compile a C probe of the header with gcc and compare sizes and offsets."""
+    fields = [f[0] for f in _lib.Problem._fields_]
+    body = "\n".join(f'  printf("{f} %zu\\n", offsetof(exattn_problem, {f}));' for f in fields)
+    prog = f"""
+#include <stdio.h>
+#include <stddef.h>
+#include "exattn.h"
+int main(void) {{
+  printf("size %zu\\n", sizeof(exattn_problem));
+{body}
+  return 0;
+}}
+"""
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "probe.c")
+        exe = os.path.join(d, "probe")
+        open(c, "w").write(prog)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()
+    vals = dict(zip(lines[::2], map(int, lines[1::2])))
+    assert vals["size"] == ctypes.sizeof(_lib.Problem)
+    for f in fields:
+        assert vals[f] == getattr(_lib.Problem, f).offset, f
+
+
+def _problem(**kw):
+    p = _lib.Problem()
+    p.dtype = 0
+    p.batch, p.seqlen_q, p.seqlen_k = 2, 100, 77
+    p.heads_q, p.heads_kv, p.head_dim = 4, 2, 128
+    p.scale = 0.088
+    D, H, Hkv = 128, 4, 2
+    p.q_stride[:] = (100 * H * D, H * D, D)
+    p.k_stride[:] = (77 * Hkv * D, Hkv * D, D)
+    p.v_stride[:] = (77 * Hkv * D, Hkv * D, D)
+    p.o_stride[:] = p.q_stride[:]
+    p.do_stride[:] = p.q_stride[:]
+    p.mask_stride[:] = (0, 0, 0, 1)
+    for k, v in kw.items():
+        if isinstance(getattr(p, k), ctypes.Array):
+            getattr(p, k)[:] = v
+        else:
+            setattr(p, k, v)
+    return p
+
+
+def test_check_accepts_valid_problem(lib):
+    assert lib.exattn_check(ctypes.byref(_problem())) == 0
+    assert lib.exattn_check(ctypes.byref(_problem(head_dim=64, q_stride=(100 * 256, 256, 64),
+                                                  k_stride=(77 * 128, 128, 64),
+                                                  v_stride=(77 * 128, 128, 64)))) == 0
+    assert lib.exattn_bwd_workspace_size(ctypes.byref(_problem())) >= 2 * 100 * 4 * 128 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=1), 2),                        # fp16 is rejected, not run as bf16
+    (dict(head_dim=96), 3),                    # only 64 and 128
+    (dict(head_dim=256), 3),
+    (dict(heads_q=6, heads_kv=4), 4),          # not a multiple
+    (dict(heads_kv=0), 4),
+    (dict(seqlen_q=-1), 4),
+    (dict(causal=2), 4),
+    (dict(scale=float("nan")), 10),
+    (dict(scale=float("inf")), 10),
+    (dict(q_stride=(0, 512, 129)), 5),         # head stride not a multiple of 8
+    (dict(k_stride=(-8, 256, 128)), 5),
+    (dict(mask_kind=3), 7),
+    (dict(mask_kind=1), 7),                    # NULL mask
+    (dict(mask_kind=1, mask=16, mask_stride=(0, 0, 77, 2)), 7),
+    (dict(mask_kind=1, mask=16, mask_stride=(-1, 0, 77, 1)), 7),
+    (dict(cu_seqlens_q=4096), 8),              # only one of the pair
+    (dict(cu_seqlens_q=4096, cu_seqlens_k=4096, num_seqs=0), 8),
+    (dict(cu_seqlens_q=4096, cu_seqlens_k=4096, num_seqs=2, max_seqlen_q=101), 8),
+    (dict(cu_seqlens_q=4096, cu_seqlens_k=4096, num_seqs=2, max_seqlen_q=10, max_seqlen_k=10,
+          mask_kind=1, mask=16), 7),           # mask + varlen
+])
+def test_check_rejects(lib, kw, status):
+    p = _problem(**kw)
+    assert lib.exattn_check(ctypes.byref(p)) == status
+    assert lib.exattn_last_error().decode() != ""
+    # the entry points reject the same problem before touching the device
+    assert lib.exattn_fwd(ctypes.byref(p), 16, 16, 16, 16, 16, None) == status
+    assert lib.exattn_bwd(ctypes.byref(p), 16, 16, 16, 16, 16, 16, 16, 16, 16, 256, 1 << 30,
+                          None) == status
+    assert lib.exattn_bwd_workspace_size(ctypes.byref(p)) == 0
+
+
+def test_null_and_alignment_rejected_before_launch(lib):
+    p = _problem()
+    assert lib.exattn_fwd(None, 16, 16, 16, 16, 16, None) == 1
+    assert lib.exattn_fwd(ctypes.byref(p), None, 16, 16, 16, 16, None) == 1
+    assert lib.exattn_fwd(ctypes.byref(p), 24, 16, 16, 16, 16, None) == 6   # q not 16-aligned
+    assert lib.exattn_fwd(ctypes.byref(p), 16, 16, 16, 16, 18, None) == 6   # lse not 4-aligned
+    ws = lib.exattn_bwd_workspace_size(ctypes.byref(p))
+    args = [16] * 9
+    assert lib.exattn_bwd(ctypes.byref(p), *args, 256, ws - 1, None) == 9   # too small
+    assert lib.exattn_bwd(ctypes.byref(p), *args, 272, ws, None) == 9       # misaligned
+    assert lib.exattn_bwd(ctypes.byref(p), *args, None, ws, None) == 9      # NULL
+    assert lib.exattn_bwd(ctypes.byref(p), 16, 16, 16, 16, 16, 16, 16, 16, 8, 256, ws, None) == 6
+
+
+def test_empty_problems_enqueue_nothing(lib):
+    """Zero rows: OK without any launch (so this runs without a GPU)."""
+    assert lib.exattn_fwd(ctypes.byref(_problem(batch=0)), None, None, None, None, None, None) == 0
+    assert lib.exattn_fwd(ctypes.byref(_problem(seqlen_q=0)), None, None, None, None, None, None) == 0
+    p = _problem(batch=0)
+    assert lib.exattn_bwd(ctypes.byref(p), *([None] * 10), 0, None) == 0
+
+
+def test_status_strings(lib):
+    for code in range(12):
+        assert lib.exattn_status_string(code).decode() not in ("", "unknown status")
+    assert lib.exattn_status_string(99).decode() == "unknown status"
+
+
+def test_timing_read_empty(lib):
+    assert lib.exattn_timing_enable(1) == 0
+    assert lib.exattn_timing_read(None, None, None, 0) == 0
+    assert lib.exattn_timing_enable(0) == 0

@@ -1,0 +1,291 @@
+"""Parity of the HIP path (called through the C ABI) against the float64 oracle.
+
+Bars: rel-L2 <= 1e-2 for out and lse, <= 2e-2 for dq, dk and dv, zero non-finite values,
+exact empty-row sentinels. Element-by-element at sizes spanning several tiles with ragged
+tails; at the full workload sizes on sampled units, rows and keys plus invariants that hold
+at any size.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_40_amd import api, workloads
+from gpu_util import compare, f64, nonfinite, run_gpu, run_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------------------------------
+# Element-by-element parity on multi-tile shapes with ragged tails
+# ------------------------------------------------------------------------------------------
+DENSE_CASES = [
+    # B, Sq, Sk, H, Hkv, D, causal
+    (2, 1000, 1000, 2, 2, 128, False),
+    (2, 1000, 1000, 2, 2, 128, True),
+    (1, 1000, 1000, 4, 2, 64, True),
+    (2, 333, 517, 2, 1, 128, False),
+    (1, 517, 333, 2, 2, 64, True),      # causal with Sq > Sk (top-left alignment)
+    (1, 300, 700, 4, 4, 128, True),     # causal with Sq < Sk
+    (1, 1, 1, 1, 1, 128, False),
+    (1, 129, 1, 2, 1, 64, False),       # a single key
+    (3, 64, 128, 8, 2, 128, False),     # exact tiles, GQA 4:1
+    (1, 257, 257, 1, 1, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=lambda c: "B{}_Sq{}_Sk{}_H{}_Hkv{}_D{}_{}".format(
+    *c[:6], "causal" if c[6] else "full"))
+def test_dense_parity(case):
+    B, Sq, Sk, H, Hkv, D, causal = case
+    p = workloads.dense(B, Sq, Sk, H, Hkv, D, seed=100 + Sq + Sk, causal=causal)
+    compare(run_gpu(p), run_oracle(p), tag=p.name + str(case))
+
+
+def test_dv_nan_repro_repeated():
+    """B1 H1 S256 D64 causal, dout = ones (flash-dmattn PR #122, "Problem"), run 10 times,
+    each time after the allocator was handed blocks full of NaN."""
+    p = workloads.dv_nan_repro()
+    ref = run_oracle(p)
+    first = None
+    for it in range(10):
+        junk = [torch.full((1 << 20,), float("nan"), device="cuda") for _ in range(8)]
+        del junk
+        g = run_gpu(p)
+        for n in ("out", "dq", "dk", "dv"):
+            assert nonfinite(g[n]) == 0, (it, n)
+        compare(g, ref, tag=f"dv_nan_repro#{it}")
+        if first is None:
+            first = g
+        else:
+            for n in ("out", "lse", "dk", "dv"):
+                assert torch.equal(g[n], first[n]), (it, n)
+
+
+@pytest.mark.parametrize("shape", workloads.PADDED_TILE_SHAPES)
+@pytest.mark.parametrize("kind", ["none", "bool", "additive", "keypad"])
+@pytest.mark.parametrize("layout", ["bshd", "bhsd"])
+def test_padded_tile_low_lse_row(shape, kind, layout):
+    """Shapes off the key tile with one query row per (b, h) whose LSE is about -111 to
+    -120 (OpenWAM PR #64, "Validation"): zero non-finite dQ (the unfixed kernel gave
+    B*H*D = 1024 per case) and oracle parity."""
+    p = workloads.padded_tile(*shape, mask_kind=kind)
+    g = run_gpu(p, layout=layout)
+    assert nonfinite(g["dq"]) == 0 and nonfinite(g["dk"]) == 0 and nonfinite(g["dv"]) == 0
+    ref = run_oracle(p)
+    compare(g, ref, tag=f"{p.name}_{layout}")
+    for b, r in p.meta["anti_rows"].items():
+        lse_row = f64(g["lse"])[b, :, r]
+        assert np.all(lse_row < -100), lse_row
+    if kind == "keypad":
+        Sk = shape[1]
+        Lb = math.ceil(0.75 * Sk)
+        # keys hidden from every query get exactly zero gradient
+        assert torch.count_nonzero(g["dk"][1, Lb:]) == 0
+        assert torch.count_nonzero(g["dv"][1, Lb:]) == 0
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_low_row_in_last_partial_query_tile(D):
+    """The low-LSE row sits in the last, partial query tile, head_dim 64 and 128."""
+    p = workloads.padded_tile(360, 77, mask_kind="bool", D=D, seed=2100 + D)
+    g = run_gpu(p)
+    assert nonfinite(g["dq"]) == 0
+    compare(g, run_oracle(p), tag=f"partial_q_tile_D{D}")
+
+
+@pytest.mark.parametrize("s", workloads.WIDE_LOGIT_SCALES)
+def test_wide_logit_small(s):
+    """k scaled by s widens the logit spread (FlyDSL PR #1033, "Repro"); multi-tile size."""
+    p = workloads.wide_logit(s, B=2, S=1000, H=2, D=128)
+    compare(run_gpu(p), run_oracle(p), tag=p.name)
+
+
+# ------------------------------------------------------------------------------------------
+# Full workload sizes: sampled units, rows and keys
+# ------------------------------------------------------------------------------------------
+
+def _unit_slices(p, b, g):
+    """Dense sub-problem holding batch b, kv head g and its query heads."""
+    grp = p.q.shape[2] // p.k.shape[2]
+    hs = slice(g * grp, (g + 1) * grp)
+    sub = workloads.Problem(p.name, p.q[b:b + 1, :, hs], p.k[b:b + 1, :, g:g + 1],
+                            p.v[b:b + 1, :, g:g + 1], p.dout[b:b + 1, :, hs], causal=p.causal,
+                            scale=p.scale)
+    return sub, hs
+
+
+@pytest.mark.parametrize("s", workloads.WIDE_LOGIT_SCALES)
+def test_wide_logit_full_size(s):
+    """B2 S8192 H32 D128 at every k scale: zero non-finite values everywhere; one full
+    (batch, head) unit compared element by element with the oracle at s in {1, 32, 64}."""
+    p = workloads.wide_logit(s)
+    g = run_gpu(p)
+    for n in ("out", "lse", "dq", "dk", "dv"):
+        assert nonfinite(g[n]) == 0, n
+    if s in (1, 32, 64):
+        b, h = 1, 5
+        sub, hs = _unit_slices(p, b, h)
+        ref = run_oracle(sub)
+        sel = {n: (slice(b, b + 1), slice(None), hs) for n in ("out", "dq")}
+        sel["lse"] = (slice(b, b + 1), hs)
+        sel.update({n: (slice(b, b + 1), slice(None), slice(h, h + 1)) for n in ("dk", "dv")})
+        gs = {n: g[n][sel[n]] for n in sel}
+        compare(gs, ref, tag=f"{p.name} unit(b={b},h={h})")
+
+
+def _varlen_sub(p, s, g):
+    """Dense view of sequence s, kv head g, of a packed problem."""
+    cq, ck = p.cu_seqlens_q.tolist(), p.cu_seqlens_k.tolist()
+    H, Hkv = p.q.shape[1], p.k.shape[1]
+    grp = H // Hkv
+    hs = slice(g * grp, (g + 1) * grp)
+    qs, qe, ks, ke = cq[s], cq[s + 1], ck[s], ck[s + 1]
+    sub = workloads.Problem(f"{p.name}_s{s}_g{g}", p.q[None, qs:qe, hs], p.k[None, ks:ke, g:g + 1],
+                            p.v[None, ks:ke, g:g + 1], p.dout[None, qs:qe, hs], causal=p.causal,
+                            scale=p.scale)
+    return sub, (qs, qe, ks, ke, hs)
+
+
+def _check_varlen(p, g, units):
+    for (s, kvh) in units:
+        sub, (qs, qe, ks, ke, hs) = _varlen_sub(p, s, kvh)
+        ref = run_oracle(sub)
+        gs = dict(out=g["out"][None, qs:qe, hs], dq=g["dq"][None, qs:qe, hs],
+                  lse=g["lse"][hs, qs:qe][None],
+                  dk=g["dk"][None, ks:ke, kvh:kvh + 1], dv=g["dv"][None, ks:ke, kvh:kvh + 1])
+        compare(gs, ref, tag=sub.name)
+    cov_q = int(p.cu_seqlens_q[-1])
+    cov_k = int(p.cu_seqlens_k[-1])
+    if cov_q < p.q.shape[0]:
+        assert torch.count_nonzero(g["out"][cov_q:]) == 0
+        assert torch.isneginf(g["lse"][:, cov_q:]).all()
+        assert torch.count_nonzero(g["dq"][cov_q:]) == 0
+    if cov_k < p.k.shape[0]:
+        assert torch.count_nonzero(g["dk"][cov_k:]) == 0
+        assert torch.count_nonzero(g["dv"][cov_k:]) == 0
+
+
+def test_varlen_gqa_full_size():
+    """16 packed sequences, lengths uniform in [128, 4096], H32 Hkv8, causal."""
+    p = workloads.varlen_gqa()
+    g = run_gpu(p)
+    for n in ("out", "lse", "dq", "dk", "dv"):
+        assert nonfinite(g[n]) == 0, n
+    _check_varlen(p, g, [(0, 0), (7, 3), (15, 7)])
+
+
+def test_varlen_uncovered_rows_written():
+    """Rows past cu_seqlens[-1] (PFCCLab cudnn-frontend PR #9, item 2): out 0, lse -inf,
+    dq/dk/dv 0, whatever the allocator held before."""
+    p = workloads.varlen_gqa(seed=4100, nseq=3, lmin=100, lmax=300, H=4, Hkv=2, extra_rows=37)
+    junk = [torch.full((1 << 22,), float("nan"), device="cuda") for _ in range(4)]
+    del junk
+    g = run_gpu(p)
+    _check_varlen(p, g, [(s, h) for s in range(3) for h in range(2)])
+
+
+@pytest.mark.parametrize("lengths", [[256], [512, 512], [300, 100, 612], [1000, 24], [1024, 1024]])
+def test_varlen_thd_shapes(lengths):
+    """The packed shapes used for the race check in PFCCLab cudnn-frontend PR #9
+    ("How it was verified"), H4 Hkv2 D128 causal, whole oracle."""
+    p = workloads.varlen_gqa(seed=4200 + sum(lengths), lengths=lengths, H=4, Hkv=2)
+    g = run_gpu(p)
+    _check_varlen(p, g, [(s, h) for s in range(len(lengths)) for h in range(2)])
+
+
+def test_long_causal_sampled():
+    """B1 S61380 H32 D128 causal: 64 sampled query rows (out, lse, dq), sampled keys near
+    the end (dk, dv), the gradient sums over all keys, zero non-finite values."""
+    p = workloads.long_causal()
+    S = p.q.shape[1]
+    g = run_gpu(p)
+    for n in ("out", "lse", "dq", "dk", "dv"):
+        assert nonfinite(g[n]) == 0, n
+    rng = np.random.default_rng(5001)
+    fixed = [0, S - 1, 127, 128, 61311, 61312]
+    rows = np.array(fixed + sorted(rng.choice(S, 58, replace=False).tolist()))
+    heads = rng.integers(0, 32, size=len(rows))
+    scale = p.softmax_scale
+    out_g, lse_g, dq_g = f64(g["out"][0]), f64(g["lse"][0]), f64(g["dq"][0])
+    ref_o, ref_l, ref_dq, got_o, got_l, got_dq = [], [], [], [], [], []
+    for h in np.unique(heads):
+        rr = rows[heads == h]
+        q = f64(p.q[0, :, h])
+        k = f64(p.k[0, :, h])
+        v = f64(p.v[0, :, h])
+        do = f64(p.dout[0, :, h])
+        o, l = oracle.rows_forward(q[rr], k, v, rr, scale, True)
+        dq = oracle.rows_backward_dq(q[rr], k, v, do[rr], rr, scale, True)
+        ref_o.append(o), ref_l.append(l), ref_dq.append(dq)
+        got_o.append(out_g[rr, h]), got_l.append(lse_g[h, rr]), got_dq.append(dq_g[rr, h])
+    from gpu_util import rel_l2, TOL
+    eo = rel_l2(np.concatenate(got_o), np.concatenate(ref_o))
+    el = rel_l2(np.concatenate(got_l), np.concatenate(ref_l))
+    ed = rel_l2(np.concatenate(got_dq), np.concatenate(ref_dq))
+    say(f"  long_causal rows: out={eo:.2e} lse={el:.2e} dq={ed:.2e}")
+    assert eo <= TOL["out"] and el <= TOL["lse"] and ed <= TOL["dq"]
+    # keys near the end: only rows at or after them can see them
+    h = 17
+    keys = np.array([S - 1, S - 2, S - 37, S - 100, S - 128, S - 129, S - 300])
+    r0 = int(keys.min())
+    q = f64(p.q[0, r0:, h])
+    do = f64(p.dout[0, r0:, h])
+    dk, dv = oracle.keys_backward(q, f64(p.k[0, :, h]), f64(p.v[0, :, h]), do, keys, scale, True,
+                                  row_offset=r0)
+    ek = rel_l2(f64(g["dk"][0, keys, h]), dk)
+    ev = rel_l2(f64(g["dv"][0, keys, h]), dv)
+    say(f"  long_causal keys: dk={ek:.2e} dv={ev:.2e}")
+    assert ek <= TOL["dk"] and ev <= TOL["dv"]
+    # sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i, per head
+    for h in (0, 31):
+        dk_sum = f64(g["dk"][0, :, h]).sum(axis=0)
+        dk_abs = np.abs(f64(g["dk"][0, :, h])).sum(axis=0)
+        assert np.all(np.abs(dk_sum) <= 2e-2 * dk_abs + 1e-3), h
+        dv_sum = f64(g["dv"][0, :, h]).sum(axis=0)
+        do_sum = f64(p.dout[0, :, h]).sum(axis=0)
+        assert rel_l2(dv_sum, do_sum) <= 2e-2, h
+
+
+# ------------------------------------------------------------------------------------------
+# Degenerate cases
+# ------------------------------------------------------------------------------------------
+
+def test_fully_masked_rows_and_uniform_scale():
+    p = workloads.dense(2, 200, 150, 2, 2, 128, seed=77)
+    keep = torch.rand(2, 1, 200, 150, generator=torch.Generator().manual_seed(1)) > 0.3
+    keep[0, 0, 5] = False           # an empty row
+    keep[1, 0, 199] = False         # an empty row in the last partial query tile
+    p.mask, p.mask_kind = keep, "bool"
+    g = run_gpu(p)
+    ref = run_oracle(p)
+    compare(g, ref, tag="empty_rows")
+    assert torch.count_nonzero(g["out"][0, 5]) == 0 and torch.count_nonzero(g["dq"][0, 5]) == 0
+    assert torch.isneginf(g["lse"][0, :, 5]).all() and torch.isneginf(g["lse"][1, :, 199]).all()
+    # scale 0: uniform attention over visible keys
+    p2 = workloads.dense(1, 130, 90, 2, 2, 64, seed=78)
+    p2.scale = 0.0
+    g2 = run_gpu(p2)
+    compare(g2, run_oracle(p2), tag="scale0")
+    np.testing.assert_allclose(f64(g2["lse"]), math.log(90), rtol=1e-6)
+
+
+def test_empty_inputs():
+    q = torch.zeros(2, 0, 4, 128, dtype=torch.bfloat16, device="cuda")
+    k = torch.randn(2, 50, 4, 128, device="cuda").bfloat16()
+    out, lse = api.exattn_fwd(q, k, k)
+    assert out.shape == (2, 0, 4, 128) and lse.shape == (2, 4, 0)
+    dq, dk, dv = api.exattn_bwd(q, k, k, out, q, lse)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dk) == 0 and torch.count_nonzero(dv) == 0
+    # no keys: every row is empty
+    q = torch.randn(1, 70, 2, 64, device="cuda").bfloat16()
+    k0 = torch.zeros(1, 0, 2, 64, dtype=torch.bfloat16, device="cuda")
+    out, lse = api.exattn_fwd(q, k0, k0)
+    dq, dk, dv = api.exattn_bwd(q, k0, k0, out, torch.randn_like(q), lse)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out) == 0 and torch.isneginf(lse).all()
+    assert torch.count_nonzero(dq) == 0
