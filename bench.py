@@ -1,0 +1,192 @@
+#!/usr/bin/env python3
+"""Throughput of the attention hot path on one MI355X.
+
+One step = one forward (exattn_fwd) and one backward (exattn_bwd: delta, main backward,
+dQ reduce) over the synthetic workload B=2, S=8192, H=32 (Hkv=32), D=128, non-causal, bf16,
+with q, k, v, dout ~ N(0,1) already resident in HBM. The FLOP count is algorithmic: 4*D
+per visible (query, key) pair for the forward and 10*D for the backward.
+
+Prints one JSON line. Per-kernel durations come from HIP events the library records
+around each of its launches on the launch stream during the timed region.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd & bwd TFLOP/s (bf16, B2 S8192 H32 D128) + % of MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz (published 2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0
+B, S, H, HKV, D = 2, 8192, 32, 32, 128
+PROFILE_PMC = os.path.join(ROOT, "profiles", "exattn_bwd_kernel_b2_s8192_h32_d128_pmc.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_attention_40_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the main backward kernel from committed PMC counters,
+    or None when the kernel sources changed since they were taken."""
+    try:
+        with open(PROFILE_PMC) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(target_seconds=15.0):
+    """The float64 oracle on a bounded sample of the same workload: whole (batch, head)
+    units of S=8192 keys, forward and backward, until about `target_seconds` elapse."""
+    import numpy as np
+
+    import oracle
+    from exact_attention_40_amd import workloads
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    rng = np.random.default_rng(9)
+    flops = 0.0
+    units = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < target_seconds and units < 8:
+        p = workloads.dense(1, S, S, 1, 1, D, seed=int(rng.integers(1 << 30)))
+        q, k, v, do = (t.double().numpy() for t in (p.q, p.k, p.v, p.dout))
+        oracle.attention_forward(q, k, v)
+        oracle.attention_backward(q, k, v, do)
+        flops += 14.0 * D * S * S
+        units += 1
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{units} whole (batch, head) units of the workload (S=8192, D=128, "
+                      f"non-causal), forward + backward in float64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from exact_attention_40_amd import api, workloads
+
+    dev = torch.device("cuda:0")
+    p = workloads.dense(B, S, S, H, HKV, D, seed=3001)
+    q, k, v, do = (t.to(dev) for t in (p.q, p.k, p.v, p.dout))
+    del p
+    stream = torch.cuda.current_stream(dev)
+    pairs = B * H * S * S
+    fwd_flops, bwd_flops = 4.0 * D * pairs, 10.0 * D * pairs
+
+    def step():
+        out, lse = api.exattn_fwd(q, k, v)
+        dq, dk, dv = api.exattn_bwd(q, k, v, out, do, lse)
+        return out, dq
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: whole steps, with per-call and per-kernel HIP events on the stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    api.timing_enable(True)
+    api.timing_read()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        out, lse = api.exattn_fwd(q, k, v)
+        ev[i][1].record(stream)
+        api.exattn_bwd(q, k, v, out, do, lse)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = api.timing_read()
+    api.timing_enable(False)
+
+    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
+    bwd_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
+    kavg = {n: ms / cnt for n, (ms, cnt) in kern.items()}
+
+    bwd_k = kavg.get("exattn_bwd_kernel", float("nan"))
+    fwd_k = kavg.get("exattn_fwd_kernel", float("nan"))
+    achieved = bwd_flops / (bwd_k * 1e-3) / 1e12
+    traffic = measured_traffic()
+    side = {}
+    for name, nbytes in (("exattn_bwd_delta_kernel", 2 * 2 * B * S * H * D + 4 * B * H * S * 3
+                          + 4 * B * S * H * D),
+                         ("exattn_bwd_dq_reduce_kernel", 4 * B * S * H * D + 2 * B * S * H * D)):
+        if name in kavg:
+            gbs = nbytes / (kavg[name] * 1e-3) / 1e9
+            side[name] = {"ms": round(kavg[name], 4), "bytes": nbytes, "GB/s": round(gbs, 1),
+                          "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 3)}
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "exact attention forward + backward, B=2 S=8192 H=32 Hkv=32 D=128, "
+                               "non-causal, bf16 in / fp32 accumulate, q,k,v,dout ~ N(0,1)",
+                   "batch": B, "seq_len": S, "heads": H, "kv_heads": HKV, "head_dim": D,
+                   "causal": False, "parallelism": "single GPU"},
+        "frac_of_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd": {"ms": round(fwd_ms, 4), "TFLOP/s": round(fwd_flops / fwd_ms / 1e9, 1),
+                "frac_of_mfma_peak": round(fwd_flops / fwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4)},
+        "bwd": {"ms": round(bwd_ms, 4), "TFLOP/s": round(bwd_flops / bwd_ms / 1e9, 1),
+                "frac_of_mfma_peak": round(bwd_flops / bwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4)},
+        "kernels_avg_ms": {n: round(t, 4) for n, t in kavg.items()},
+        "fwd_kernel_TFLOP/s": round(fwd_flops / (fwd_k * 1e-3) / 1e12, 1),
+        "side_passes": side,
+        "roofline": {"kernel": "exattn_bwd_kernel", "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "algorithmic_flops_per_launch": bwd_flops},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

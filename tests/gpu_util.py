@@ -104,3 +104,54 @@ def compare(gpu, ref, names=("out", "lse", "dq", "dk", "dv"), select=None, tag="
         assert e <= TOL[n], f"{tag} {n}: rel-L2 {e:.3e} > {TOL[n]:.0e}"
     say(f"  {tag} " + " ".join(f"{n}={e:.2e}" for n, e in report.items()))
     return report
+
+
+def dq_reassociation_bound(p, block_n=128):
+    """Per-element bound on run-to-run differences of dq (float64 numpy, dq's layout).
+
+    dq sums one fp32 partial per block of `block_n` keys with atomics, so two runs differ
+    only by the order of those additions. For N terms that is at most
+    (N - 1) * 2**-24 * sum_i |t_i| (PFCCLab cudnn-frontend PR #9, "How it was verified"),
+    and sum_i |t_i| <= scale * sum_j |dS_ij k_jd|; dS comes from the float64 oracle.
+    Dense problems only.
+    """
+    q, k, v, do = f64(p.q), f64(p.k), f64(p.v), f64(p.dout)
+    B, Sq, H, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    scale = p.softmax_scale
+    nblk = max(1, -(-Sk // block_n))
+    bound = np.zeros_like(q)
+    m = oracle_mask(p)
+    for b in range(B):
+        for h in range(H):
+            g = h // (H // Hkv)
+            keep = bias = None
+            if m is not None:
+                mm = m
+                while mm.ndim < 4:
+                    mm = mm[None]
+                mb = np.broadcast_to(mm[b if mm.shape[0] > 1 else 0, h if mm.shape[1] > 1 else 0],
+                                     (Sq, Sk))
+                if p.mask_kind == "bool":
+                    keep = mb.astype(bool)
+                else:
+                    bias = mb.astype(np.float64)
+            vis = oracle.visibility(Sq, Sk, p.causal, keep, bias)
+            out, _, P = oracle.unit_forward(q[b, :, h], k[b, :, g], v[b, :, g], scale, vis, bias)
+            dP = do[b, :, h] @ v[b, :, g].T
+            dS = P * (dP - np.sum(do[b, :, h] * out, axis=1)[:, None])
+            bound[b, :, h] = (nblk - 1) * 2.0 ** -24 * scale * (np.abs(dS) @ np.abs(k[b, :, g]))
+    return bound
+
+
+def dq_runs_agree(a, b, bound):
+    """|a - b| <= bound + one bf16 ulp of max(|a|, |b|); reports the worst ratio."""
+    a64, b64 = f64(a), f64(b)
+    mag = np.maximum(np.abs(a64), np.abs(b64))
+    ulp = np.where(mag > 0, 2.0 ** (np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - 7), 0.0)
+    diff = np.abs(a64 - b64)
+    lim = bound + ulp
+    worst = float(np.max(diff / np.where(lim > 0, lim, 1e-300))) if diff.size else 0.0
+    say(f"  dq run-to-run: {int((diff > 0).sum())} of {diff.size} elements differ, "
+        f"worst diff/bound = {worst:.3f}")
+    return bool(np.all(diff <= lim))
