@@ -29,7 +29,7 @@ MASK_NONE, MASK_BOOL_U8, MASK_ADD_BF16 = 0, 1, 2
 EXPORTED = (
     "exattn_abi_version", "exattn_check", "exattn_fwd", "exattn_bwd_workspace_size",
     "exattn_bwd", "exattn_status_string", "exattn_last_error", "exattn_timing_enable",
-    "exattn_timing_read",
+    "exattn_timing_read", "exattn_set_variant",
 )
 
 _i32, _i64, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
@@ -85,6 +85,8 @@ def load():
         lib.exattn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_char_p),
                                            ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_int), ctypes.c_int]
+        lib.exattn_set_variant.restype = ctypes.c_int
+        lib.exattn_set_variant.argtypes = [ctypes.c_int, ctypes.c_int]
         v = lib.exattn_abi_version()
         if v != ABI_VERSION:
             raise RuntimeError(f"libexattn ABI version {v}, binding expects {ABI_VERSION}")

@@ -20,7 +20,7 @@ import torch
 from . import _lib
 
 __all__ = ["exattn_fwd", "exattn_bwd", "exattn_check", "attn_fwd", "attn_bwd", "attention",
-           "AttnFunction", "timing_enable", "timing_read", "workspace_size"]
+           "AttnFunction", "timing_enable", "timing_read", "workspace_size", "set_variant"]
 
 
 def _fail(lib, status):
@@ -323,6 +323,14 @@ def attention(q, k, v, causal=False, scale=None, mask=None, cu_seqlens_q=None,
     """Differentiable attention output (bf16)."""
     return AttnFunction.apply(q, k, v, causal, scale, mask, cu_seqlens_q, cu_seqlens_k,
                               max_seqlen_q, max_seqlen_k)
+
+
+def set_variant(kernel: int, variant: int):
+    """Select a compiled tiling (see exattn_set_variant in include/exattn.h)."""
+    lib = _lib.load()
+    st = lib.exattn_set_variant(int(kernel), int(variant))
+    if st != _lib.OK:
+        _fail(lib, st)
 
 
 def timing_enable(on: bool = True):

@@ -275,7 +275,7 @@ exattn_status exattn_fwd(const exattn_problem* p, const void* q, const void* k, 
   a.Hkv = p->heads_kv;
   a.group = H / p->heads_kv;
   a.num_units = g.units;
-  const int bm = fwd_block_m(D);
+  const int bm = fwd_block_m(D, p->mask_kind, g.varlen);
   const int maxq = g.varlen ? p->max_seqlen_q : p->seqlen_q;
   a.num_q_tiles = (maxq + bm - 1) / bm;
   a.lse_row = p->seqlen_q;
@@ -391,6 +391,15 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
     if (e != hipSuccess) return hip_fail(e, "kv tail launch");
   }
   return EXATTN_OK;
+}
+
+exattn_status exattn_set_variant(int kernel, int variant) {
+  g_err[0] = 0;
+  if (kernel == 0 && variant >= 0 && variant <= 3) {
+    set_fwd_variant(variant);
+    return EXATTN_OK;
+  }
+  return fail(EXATTN_ERR_SHAPE, "unknown kernel %d or variant %d", kernel, variant);
 }
 
 exattn_status exattn_timing_enable(int enable) {

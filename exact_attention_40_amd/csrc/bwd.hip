@@ -20,10 +20,15 @@
 // dense indexer", item 2); exponent bounded above (same page, item 3): exp2 of min(x, 0),
 // since s - lse <= 0 for a consistent LSE.
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "params.hpp"
 
 namespace exattn {
+
+template <bool B>
+using bool_c = std::integral_constant<bool, B>;
 
 // ----------------------------------------------------------------------------------------
 // 1. Delta / lse2 / dQ-accumulator clear. One group of D/8 lanes per (row, head).
@@ -69,52 +74,115 @@ __global__ void __launch_bounds__(256) delta_kernel(BwdArgs a) {
 // 2. Main backward kernel.
 //
 // One workgroup = 4 waves = 128 keys of one (unit, kv head); wave w owns keys 32w..32w+31
-// and keeps their K and V fragments (B-operand layout, k-slots = d) in registers, plus
-// fp32 dK and dV accumulators (C layout: rows = keys, columns = d).
-// Per query tile of 64 rows, staged in LDS both row-major (A operand, k = d) and
-// row-interleaved Q[row/4][d][row%4] (B operand with k = rows):
+// and accumulates their dK and dV in fp32 (C layout: rows = keys, columns = d) across
+// every query head of the group and every query tile that can see the block. The
+// block's K and V stay in LDS for the whole loop. Per query tile of 64 rows, Q and dO are
+// copied straight from global memory into LDS (double-buffered, zero past the end), and
+// lse2/Delta through registers:
 //   S  = Q K^T and dP = dO V^T          (lane = key column, registers = query rows)
-//   P  = exp2(min(S*c - lse2, 0)), dS = P * (dP - Delta), masked entries 0
-//   dV += P^T dO, dK += dS^T Q          (P and dS feed the A operand from registers)
-//   dS -> LDS [query][key]; dQ tile = dS K over all 128 keys, K read from an interleaved
-//   copy K[key/4][d][key%4]; each wave adds its dQ tiles with fp32 atomics.
+//   P  = exp2(min(S*c + bias - lse2, 0)), dS = P * (dP - Delta); hidden entries are 0
+//   dV += P^T dO, dK += dS^T Q          (P and dS are the A operand straight from registers;
+//                                        dO and Q come from transposed LDS reads)
+//   dS -> LDS [query][key]; each wave forms 32x32 dQ tiles over the block's 128 keys
+//   (K from transposed LDS reads) and adds them to the fp32 accumulator with buffer
+//   atomics, which drop rows past the end of the sequence.
+// Row-major LDS tiles without padding use an XOR swizzle of their 16-byte chunks,
+// chunk' = chunk ^ (2*(row & 3) + ((row >> 2) & 1)), which keeps both the 16-byte row reads
+// and the 8-byte transposed reads free of bank conflicts.
 // ----------------------------------------------------------------------------------------
 template <int D>
 struct BwdTile {
   static constexpr int NW = 4;
+  static constexpr int NT = 64 * NW;
   static constexpr int BN = 128;
   static constexpr int BM = 64;
   static constexpr int QB = BM / 32;
   static constexpr int DS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int QLD = D + 8;        // row-major pitch
-  static constexpr int TG = D * 4 + 8;     // interleaved 4-row group pitch
-  static constexpr int SLD = BN + 8;       // dS pitch
-  static constexpr int Q_ELEMS = BM * QLD;
-  static constexpr int QT_ELEMS = (BM / 4) * TG;
-  static constexpr int KT_ELEMS = (BN / 4) * TG;
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int SLD = BN + 8;             // dS pitch (16 B mod 128 B)
+  static constexpr int Q_ELEMS = BM * D;
+  static constexpr int K_ELEMS = BN * D;
   static constexpr int S_ELEMS = BM * SLD;
-  static constexpr int QGR = (BM / 4) * (D / 8);   // 4x8 blocks per Q tile
-  static constexpr int KGR = (BN / 4) * (D / 8);   // 4x8 blocks of the K tile
-  static constexpr int DQ_TILES = QB * DB;         // 32x32 dQ tiles per query tile
+  static constexpr int DQ_TILES = QB * DB;       // 32x32 dQ tiles per query tile
   static constexpr int DQ_PER_WAVE = DQ_TILES / NW;
+  static_assert((BM * CPR) % (64 * NW) == 0 && (BN * CPR) % (64 * NW) == 0, "even copy split");
+  static_assert(DQ_PER_WAVE * NW == DQ_TILES, "even dQ split");
 };
+
+__device__ __forceinline__ int swz_f(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
+
+// Element offset of (row, col) in a swizzled row-major tile with D columns.
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+  return row * D + ((((col >> 3) ^ swz_f(row))) << 3) + (col & 7);
+}
+
+// Copy R rows of D bf16 (row stride `stride` elements, rows past the buffer range read as
+// zero) into a swizzled LDS tile with direct global->LDS loads: each wave instruction
+// fills 64 consecutive 16-byte LDS chunks, lane i the i-th, so lane i fetches the global
+// chunk that the swizzle places there. Completion is tracked by vmcnt.
+template <int D, int R, int NW>
+__device__ __forceinline__ void copy_tile_to_lds(bf16* dst, __amdgpu_buffer_rsrc_t rs, int stride,
+                                                 int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int ITER = R * CPR / 64 / NW;
+#pragma unroll
+  for (int i = 0; i < ITER; ++i) {
+    const int p0 = (i * NW + wave) * 64;
+    const int pos = p0 + lane;
+    const int row = pos / CPR, pc = pos % CPR;
+    const int col = (pc ^ swz_f(row)) * 8;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(dst + p0 * 8), 16,
+        (int)((row * stride + col) * 2), 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wait for every vector-memory operation except the most recent N. The counter retires in
+// issue order, so this waits for the earlier loads while the last N (the dQ atomics of the
+// current tile) stay in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem_except() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int D>
+constexpr size_t bwd_smem_bytes() {
+  using T = BwdTile<D>;
+  return (size_t)(2 * T::K_ELEMS + 4 * T::Q_ELEMS + T::S_ELEMS) * 2 + 4 * T::BM * sizeof(float);
+}
+
+// LDS read at a per-lane byte address plus a compile-time byte offset (the offset folds into
+// the instruction's immediate field).
+template <class V>
+__device__ __forceinline__ V lds_at(const unsigned char* base, int imm) {
+  return *reinterpret_cast<const V*>(base + imm);
+}
+__device__ __forceinline__ bf16x4 tr_at(const unsigned char* base, int imm) {
+  return lds_read_tr4(reinterpret_cast<const bf16*>(base + imm));
+}
 
 template <int D, bool CAUSAL, int MASK, bool VARLEN>
 __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
   using T = BwdTile<D>;
+  constexpr int RB = D * 2;                      // bytes per swizzled row
+  constexpr int QBYTES = T::Q_ELEMS * 2;         // one Q or dO buffer
+  constexpr int KBYTES = T::K_ELEMS * 2;
+  constexpr int DO_OFF = 2 * QBYTES;             // dO buffers follow the two Q buffers
+  constexpr int V_OFF = KBYTES;                  // V follows K
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  bf16* q_l = reinterpret_cast<bf16*>(smem);
-  bf16* qt_l = q_l + T::Q_ELEMS;
-  bf16* do_l = qt_l + T::QT_ELEMS;
-  bf16* dot_l = do_l + T::Q_ELEMS;
-  bf16* kt_l = dot_l + T::QT_ELEMS;
-  bf16* ds_l = kt_l + T::KT_ELEMS;
-  float* lse2_l = reinterpret_cast<float*>(ds_l + T::S_ELEMS);
-  float* del_l = lse2_l + T::BM;
+  unsigned char* k_b = smem;                     // K then V
+  unsigned char* q_b = smem + 2 * KBYTES;        // Q[2] then dO[2]
+  unsigned char* ds_b = q_b + 4 * QBYTES;        // dS [BM][SLD]
+  float* lse2_l = reinterpret_cast<float*>(ds_b + T::S_ELEMS * 2);  // [2][BM]
+  float* del_l = lse2_l + 2 * T::BM;                                // [2][BM]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int half = lane >> 5, l32 = lane & 31;
+  const int half = lane >> 5, l32 = lane & 31, grp = lane >> 4, j16 = lane & 15;
 
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int kbi = blk % a.num_k_blocks;
@@ -122,8 +190,7 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
   const int g = ug % a.Hkv, unit = ug / a.Hkv;
 
   int Sq, Sk;
-  int64_t qrow0, krow0;              // first row of the unit in the token dimension
-  int64_t qb_off, kb_off, vb_off, ob_off, dob_off, st_base_unit;
+  int64_t qrow0, krow0, qb_off, kb_off, vb_off, dob_off, st_unit;
   if constexpr (VARLEN) {
     const int qs = a.cu_q[unit], ks = a.cu_k[unit];
     Sq = a.cu_q[unit + 1] - qs;
@@ -134,8 +201,7 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
     kb_off = (int64_t)ks * a.k_ss;
     vb_off = (int64_t)ks * a.v_ss;
     dob_off = (int64_t)qs * a.do_ss;
-    ob_off = 0;
-    st_base_unit = qs;
+    st_unit = qs;
   } else {
     Sq = a.Sq;
     Sk = a.Sk;
@@ -145,43 +211,65 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
     kb_off = (int64_t)unit * a.k_sb;
     vb_off = (int64_t)unit * a.v_sb;
     dob_off = (int64_t)unit * a.do_sb;
-    ob_off = 0;
-    st_base_unit = 0;
+    st_unit = 0;
   }
-  (void)ob_off;
   const int kb0 = kbi * T::BN;
   if (kb0 >= Sk) return;
+  const int krows = min(T::BN, Sk - kb0);
 
-  const bf16* K = reinterpret_cast<const bf16*>(a.k) + kb_off + (int64_t)g * a.k_sh;
-  const bf16* V = reinterpret_cast<const bf16*>(a.v) + vb_off + (int64_t)g * a.v_sh;
-
-  // This wave's key fragments (B operand: column = key, k-slots = d).
-  const int kw = kb0 + wave * 32 + l32;
-  bf16x8 kf[T::DS], vf[T::DS];
-  if (kw < Sk) {
-    const bf16* kr = K + (int64_t)kw * a.k_ss + 8 * half;
-    const bf16* vr = V + (int64_t)kw * a.v_ss + 8 * half;
-#pragma unroll
-    for (int s = 0; s < T::DS; ++s) {
-      kf[s] = *reinterpret_cast<const bf16x8*>(kr + 16 * s);
-      vf[s] = *reinterpret_cast<const bf16x8*>(vr + 16 * s);
-    }
-  } else {
-#pragma unroll
-    for (int s = 0; s < T::DS; ++s) kf[s] = vf[s] = bf16x8{};
+  // The block's K and V, row-major and swizzled, zero past the last key.
+  {
+    const bf16* K = reinterpret_cast<const bf16*>(a.k) + kb_off + (int64_t)g * a.k_sh +
+                    (int64_t)kb0 * a.k_ss;
+    const bf16* V = reinterpret_cast<const bf16*>(a.v) + vb_off + (int64_t)g * a.v_sh +
+                    (int64_t)kb0 * a.v_ss;
+    copy_tile_to_lds<D, T::BN, T::NW>(reinterpret_cast<bf16*>(k_b),
+                                     make_rsrc(K, (uint32_t)((krows - 1) * a.k_ss + D) * 2u),
+                                     (int)a.k_ss, wave, lane);
+    copy_tile_to_lds<D, T::BN, T::NW>(reinterpret_cast<bf16*>(k_b + V_OFF),
+                                     make_rsrc(V, (uint32_t)((krows - 1) * a.v_ss + D) * 2u),
+                                     (int)a.v_ss, wave, lane);
   }
+  const int kl_w = wave * 32 + l32;          // block-local key of this lane
+  const int kw = kb0 + kl_w;
 
-  // Interleaved copy of the whole 128-key K block for the dQ product.
-  for (int gi = tid; gi < T::KGR; gi += 256) {
-    const int g4 = gi / (D / 8), d8 = gi % (D / 8);
-    u32x4 rr[4];
+  // ---- per-lane LDS base addresses; everything else is an immediate offset ----------------
+  // Row-operand reads (row & 7 == l32 & 7 for Q/dO rows qb*32+l32 and K/V rows kl_w): the
+  // swizzle only permutes d-slab pairs within groups of four, so four bases cover all slabs.
+  const int fa_hi = l32 & 3, fa_lo = (l32 >> 2) & 1;
+  const unsigned char* aq[4];   // Q buffer 0 (+QBYTES for buffer 1, +DO_OFF for dO)
+  const unsigned char* ak[4];   // K (+V_OFF for V)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kb0 + 4 * g4 + i;
-      rr[i] = key < Sk ? ldg16(K + (int64_t)key * a.k_ss + d8 * 8) : u32x4{0, 0, 0, 0};
-    }
-    store_4x8_transposed(kt_l + g4 * T::TG + d8 * 32, rr[0], rr[1], rr[2], rr[3]);
+  for (int i = 0; i < 4; ++i) {
+    const int off = 32 * (i ^ fa_hi) + 16 * (half ^ fa_lo);
+    aq[i] = q_b + l32 * RB + off;
+    ak[i] = k_b + kl_w * RB + off;
   }
+  // Transposed reads of Q/dO for dV/dK: rows 16kk + 4*half + (j16>>2) (+8), columns
+  // db*32 + 16*(grp&1) + 4*(j16&3). Two bases, for db even and odd.
+  const int tr_row = j16 >> 2;
+  const int clow = 2 * (grp & 1) + ((j16 & 3) >> 1);
+  const unsigned char* tq[2];
+  {
+    const int row = 4 * half + tr_row;
+    const int f = swz_f(row);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) tq[b] = q_b + row * RB + 16 * ((4 * b + clow) ^ f) + 8 * (j16 & 1);
+  }
+  // Transposed reads of K for dQ: rows 16kk + 8*half + (j16>>2) and 4 rows below.
+  const unsigned char* tk[2][2];
+#pragma unroll
+  for (int sec = 0; sec < 2; ++sec) {
+    const int row = 8 * half + tr_row + 4 * sec;
+    const int f = swz_f(row);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+      tk[sec][b] = k_b + row * RB + 16 * ((4 * b + clow) ^ f) + 8 * (j16 & 1);
+  }
+  // dS written as [query][key] from the C layout, read back as 8 consecutive keys per lane.
+  unsigned char* dsw = ds_b + (4 * half * T::SLD + kl_w) * 2;
+  const unsigned char* dsr = ds_b + (l32 * T::SLD + 8 * half) * 2;
+  const unsigned char* st_rd = reinterpret_cast<const unsigned char*>(lse2_l) + 16 * half;
 
   f32x16 dk[T::DB], dv[T::DB];
 #pragma unroll
@@ -190,169 +278,189 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
   const float c2 = a.scale_log2;
   const uint8_t* mask_u8 = reinterpret_cast<const uint8_t*>(a.mask);
   const bf16* mask_bf = reinterpret_cast<const bf16*>(a.mask);
-  const int qstart = CAUSAL ? (kb0 / T::BM) * T::BM : 0;
-  const bool q_thread = (T::QGR >= 256) || (tid < T::QGR);
-  const int sg4 = tid / (D / 8), sd8 = tid % (D / 8);
+  const int qstart = CAUSAL ? min(kb0 / T::BM * T::BM, Sq) : 0;
+  const int n_qt = (Sq - qstart + T::BM - 1) / T::BM;
+  const int n_iter = a.group * n_qt;
 
-  for (int hh = 0; hh < a.group; ++hh) {
-    const int head = g * a.group + hh;
-    const bf16* Q = reinterpret_cast<const bf16*>(a.q) + qb_off + (int64_t)head * a.q_sh;
-    const bf16* DO = reinterpret_cast<const bf16*>(a.dout) + dob_off + (int64_t)head * a.do_sh;
-    const int64_t st_base = VARLEN ? (int64_t)head * a.lse_row + st_base_unit
-                                   : ((int64_t)unit * a.H + head) * a.Sq;
+  // Staging of one query tile: Q and dO straight into LDS, lse2 and Delta via registers.
+  float st_v = 0.f;
+  auto tile_head = [&](int it) { return g * a.group + it / n_qt; };
+  auto tile_q0 = [&](int it) { return qstart + (it % n_qt) * T::BM; };
+  auto load_q = [&](int it, int buf) {
+    const int head = tile_head(it), qt0 = tile_q0(it);
+    const int rows = min(T::BM, Sq - qt0);
+    const bf16* Qp = reinterpret_cast<const bf16*>(a.q) + qb_off + (int64_t)head * a.q_sh +
+                     (int64_t)qt0 * a.q_ss;
+    const bf16* Dp = reinterpret_cast<const bf16*>(a.dout) + dob_off + (int64_t)head * a.do_sh +
+                     (int64_t)qt0 * a.do_ss;
+    copy_tile_to_lds<D, T::BM, T::NW>(reinterpret_cast<bf16*>(q_b + buf * QBYTES),
+                                     make_rsrc(Qp, (uint32_t)((rows - 1) * a.q_ss + D) * 2u),
+                                     (int)a.q_ss, wave, lane);
+    copy_tile_to_lds<D, T::BM, T::NW>(reinterpret_cast<bf16*>(q_b + DO_OFF + buf * QBYTES),
+                                     make_rsrc(Dp, (uint32_t)((rows - 1) * a.do_ss + D) * 2u),
+                                     (int)a.do_ss, wave, lane);
+    const int64_t st = VARLEN ? (int64_t)head * a.lse_row + st_unit
+                              : ((int64_t)unit * a.H + head) * a.Sq;
+    if (tid < 2 * T::BM) {
+      const int r = tid & (T::BM - 1);
+      const bool ok = r < rows;
+      st_v = tid < T::BM ? (ok ? a.lse2[st + qt0 + r] : INFINITY) : (ok ? a.delta[st + qt0 + r] : 0.f);
+    }
+  };
+  auto store_stats = [&](int buf) {
+    if (tid < T::BM) lse2_l[buf * T::BM + tid] = st_v;
+    else if (tid < 2 * T::BM) del_l[buf * T::BM + tid - T::BM] = st_v;
+  };
+
+  if (n_iter > 0) {
+    load_q(0, 0);
+    store_stats(0);
+  }
+  wait_vmem();
+  __syncthreads();
+
+  // One query tile. BUF (0/1) selects the staging buffer at compile time.
+  auto iteration = [&](int it, auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    constexpr int QO = BUF * QBYTES;
+    if (it + 1 < n_iter) load_q(it + 1, BUF ^ 1);
+    const int head = tile_head(it), qt0 = tile_q0(it);
+    const bool edge = (kb0 + T::BN > Sk) || (qt0 + T::BM > Sq) || (MASK != kMaskNone) ||
+                      (CAUSAL && kb0 + T::BN - 1 > qt0);
     const int64_t m_base = (int64_t)unit * a.m_sb + (int64_t)head * a.m_sh;
 
-    for (int qt0 = qstart; qt0 < Sq; qt0 += T::BM) {
-      __syncthreads();  // previous tile's LDS reads are complete
-      if (q_thread) {
-        u32x4 rq[4], rd[4];
+    // P = exp2(min(S*c + bias - lse2, 0)) and dS = P * (dP - Delta), in place.
+    auto softmax_grad = [&](f32x16& s, f32x16& dp, int qb, auto edge_tag) {
+      constexpr bool EDGE = decltype(edge_tag)::value;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int qi = qt0 + 4 * sg4 + i;
-          const bool ok = qi < Sq;
-          rq[i] = ok ? ldg16(Q + (int64_t)qi * a.q_ss + sd8 * 8) : u32x4{0, 0, 0, 0};
-          rd[i] = ok ? ldg16(DO + (int64_t)qi * a.do_ss + sd8 * 8) : u32x4{0, 0, 0, 0};
-        }
+      for (int rg = 0; rg < 4; ++rg) {
+        const int soff = BUF * T::BM * 4 + (qb * 32 + 8 * rg) * 4;
+        const f32x4 l2 = lds_at<f32x4>(st_rd, soff);
+        const f32x4 dd = lds_at<f32x4>(st_rd, soff + 2 * T::BM * 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<u32x4*>(q_l + (4 * sg4 + i) * T::QLD + sd8 * 8) = rq[i];
-          *reinterpret_cast<u32x4*>(do_l + (4 * sg4 + i) * T::QLD + sd8 * 8) = rd[i];
-        }
-        store_4x8_transposed(qt_l + sg4 * T::TG + sd8 * 32, rq[0], rq[1], rq[2], rq[3]);
-        store_4x8_transposed(dot_l + sg4 * T::TG + sd8 * 32, rd[0], rd[1], rd[2], rd[3]);
-      }
-      if (tid < T::BM) {
-        const int qi = qt0 + tid;
-        lse2_l[tid] = qi < Sq ? a.lse2[st_base + qi] : INFINITY;
-      } else if (tid < 2 * T::BM) {
-        const int qi = qt0 + tid - T::BM;
-        del_l[tid - T::BM] = qi < Sq ? a.delta[st_base + qi] : 0.f;
-      }
-      __syncthreads();
-
-      // S = Q K^T and dP = dO V^T: rows = queries, columns = this wave's keys.
-      f32x16 s[T::QB], dp[T::QB];
-#pragma unroll
-      for (int qb = 0; qb < T::QB; ++qb) s[qb] = dp[qb] = f32x16{};
-#pragma unroll
-      for (int ds = 0; ds < T::DS; ++ds) {
-#pragma unroll
-        for (int qb = 0; qb < T::QB; ++qb) {
-          const int off = (qb * 32 + l32) * T::QLD + ds * 16 + 8 * half;
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(q_l + off);
-          const bf16x8 da = *reinterpret_cast<const bf16x8*>(do_l + off);
-          s[qb] = mfma32(qa, kf[ds], s[qb]);
-          dp[qb] = mfma32(da, vf[ds], dp[qb]);
-        }
-      }
-
-      // P and dS in place.
-      const bool edge = (kb0 + T::BN > Sk) || (qt0 + T::BM > Sq) || (MASK != kMaskNone) ||
-                        (CAUSAL && kb0 + T::BN - 1 > qt0);
-#pragma unroll
-      for (int qb = 0; qb < T::QB; ++qb) {
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int rl = qb * 32 + 8 * rg + 4 * half;  // local row of register 4*rg
-          const f32x4 l2 = *reinterpret_cast<const f32x4*>(lse2_l + rl);
-          const f32x4 dl = *reinterpret_cast<const f32x4*>(del_l + rl);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rg + e;
-            float x = s[qb][r] * c2;
-            bool vis = true;
-            if (edge) {
-              const int qi = qt0 + rl + e;
-              vis = (qi < Sq) && (kw < Sk);
-              if (CAUSAL) vis = vis && (kw <= qi);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rg + e;
+          float p;
+          if constexpr (!EDGE) {
+            p = fast_exp2(fminf(fmaf(s[r], c2, -l2[e]), 0.f));
+          } else {
+            // Branch-free visibility: mask reads use indices clamped into range.
+            const int qi = qt0 + qb * 32 + 8 * rg + 4 * half + e;
+            bool vis = (qi < Sq) && (kw < Sk);
+            if (CAUSAL) vis = vis && (kw <= qi);
+            float b2 = 0.f;
+            if (MASK != kMaskNone) {
+              const int64_t mi = m_base + (int64_t)min(qi, Sq - 1) * a.m_si + min(kw, Sk - 1);
               if (MASK == kMaskBool) {
-                if (vis) vis = mask_u8[m_base + (int64_t)qi * a.m_si + kw] != 0;
-              }
-              if (MASK == kMaskAdd) {
-                if (vis) x = x + (float)mask_bf[m_base + (int64_t)qi * a.m_si + kw] * kLog2e;
+                vis = vis && (mask_u8[mi] != 0);
+              } else {
+                const float bias = (float)mask_bf[mi];
+                vis = vis && (bias != -INFINITY);
+                b2 = vis ? bias * kLog2e : 0.f;
               }
             }
-            const float p = vis ? fast_exp2(fminf(x - l2[e], 0.f)) : 0.f;
-            s[qb][r] = p;
-            dp[qb][r] = p * (dp[qb][r] - dl[e]);
+            const float e2 = fast_exp2(fminf(fmaf(s[r], c2, b2 - l2[e]), 0.f));
+            p = vis ? e2 : 0.f;
           }
+          s[r] = p;
+          dp[r] = p * (dp[r] - dd[e]);
         }
       }
+    };
 
-      // dV += P^T dO and dK += dS^T Q over 16-row slabs of the query tile.
 #pragma unroll
-      for (int kk = 0; kk < T::BM / 16; ++kk) {
-        const int qb = kk >> 1, hs = (kk & 1) * 8;
-        const bf16x8 pa = cvt8(s[qb][hs + 0], s[qb][hs + 1], s[qb][hs + 2], s[qb][hs + 3],
-                               s[qb][hs + 4], s[qb][hs + 5], s[qb][hs + 6], s[qb][hs + 7]);
-        const bf16x8 sa = cvt8(dp[qb][hs + 0], dp[qb][hs + 1], dp[qb][hs + 2], dp[qb][hs + 3],
-                               dp[qb][hs + 4], dp[qb][hs + 5], dp[qb][hs + 6], dp[qb][hs + 7]);
+    for (int qb = 0; qb < T::QB; ++qb) {
+      // S = Q K^T and dP = dO V^T for 32 query rows: rows = queries, columns = keys.
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ds = 0; ds < T::DS; ++ds) {
+        const int i = ds & 3, m = (ds >> 2) * 128;
+        const bf16x8 kf = lds_at<bf16x8>(ak[i], m);
+        const bf16x8 vf = lds_at<bf16x8>(ak[i], m + V_OFF);
+        s = mfma32(lds_at<bf16x8>(aq[i], QO + qb * 32 * RB + m), kf, s);
+        dp = mfma32(lds_at<bf16x8>(aq[i], DO_OFF + QO + qb * 32 * RB + m), vf, dp);
+      }
+      if (edge) softmax_grad(s, dp, qb, bool_c<true>{});
+      else softmax_grad(s, dp, qb, bool_c<false>{});
+      // dV += P^T dO and dK += dS^T Q over the two 16-row slabs of these 32 rows.
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int kk = 2 * qb + ks, hs = ks * 8;
+        const bf16x8 pa = cvt8(s[hs + 0], s[hs + 1], s[hs + 2], s[hs + 3], s[hs + 4], s[hs + 5],
+                               s[hs + 6], s[hs + 7]);
+        const bf16x8 sa = cvt8(dp[hs + 0], dp[hs + 1], dp[hs + 2], dp[hs + 3], dp[hs + 4],
+                               dp[hs + 5], dp[hs + 6], dp[hs + 7]);
 #pragma unroll
         for (int db = 0; db < T::DB; ++db) {
-          const int off = (4 * kk + half) * T::TG + (db * 32 + l32) * 4;
-          const bf16x8 ob = cat44(*reinterpret_cast<const bf16x4*>(dot_l + off),
-                                  *reinterpret_cast<const bf16x4*>(dot_l + off + 2 * T::TG));
-          const bf16x8 qbv = cat44(*reinterpret_cast<const bf16x4*>(qt_l + off),
-                                   *reinterpret_cast<const bf16x4*>(qt_l + off + 2 * T::TG));
+          const unsigned char* tb = tq[db & 1];
+          const int o = QO + 16 * kk * RB + 128 * (db >> 1);
+          const bf16x8 ob = cat44(tr_at(tb, DO_OFF + o), tr_at(tb, DO_OFF + o + 8 * RB));
+          const bf16x8 qv = cat44(tr_at(tb, o), tr_at(tb, o + 8 * RB));
           dv[db] = mfma32(pa, ob, dv[db]);
-          dk[db] = mfma32(sa, qbv, dk[db]);
+          dk[db] = mfma32(sa, qv, dk[db]);
         }
       }
-
       // dS -> LDS as [query][key] for the dQ product.
 #pragma unroll
-      for (int qb = 0; qb < T::QB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          ds_l[(qb * 32 + acc_row(r, half)) * T::SLD + wave * 32 + l32] = (bf16)dp[qb][r];
-      __syncthreads();
+      for (int r = 0; r < 16; ++r)
+        *reinterpret_cast<bf16*>(dsw + (qb * 32 + 8 * (r >> 2) + (r & 3)) * T::SLD * 2) = (bf16)dp[r];
+    }
+    __syncthreads();  // dS complete; every wave is done with this tile's Q and dO
 
-      // dQ tiles: rows = queries, columns = d; k = the block's 128 keys.
+    // dQ tiles: rows = queries, columns = d; k = the block's 128 keys.
+    const int qrows = min(T::BM, Sq - qt0);
+    float* dqp = a.dq_acc + ((qrow0 + qt0) * a.H + head) * D;
+    const auto rdq = make_rsrc(dqp, (uint32_t)((qrows - 1) * a.H * D + D) * 4u);
 #pragma unroll
-      for (int tt = 0; tt < T::DQ_PER_WAVE; ++tt) {
-        const int tile = wave * T::DQ_PER_WAVE + tt;
-        const int qb = tile / T::DB, db = tile % T::DB;
-        f32x16 acc = f32x16{};
+    for (int tt = 0; tt < T::DQ_PER_WAVE; ++tt) {
+      const int tile = wave * T::DQ_PER_WAVE + tt;
+      const int qb = tile / T::DB, db = tile % T::DB;
+      f32x16 acc = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < T::BN / 16; ++kk) {
-          const bf16x8 sa =
-              *reinterpret_cast<const bf16x8*>(ds_l + (qb * 32 + l32) * T::SLD + kk * 16 + 8 * half);
-          const int off = (4 * kk + 2 * half) * T::TG + (db * 32 + l32) * 4;
-          const bf16x8 kbv = cat44(*reinterpret_cast<const bf16x4*>(kt_l + off),
-                                   *reinterpret_cast<const bf16x4*>(kt_l + off + T::TG));
-          acc = mfma32(sa, kbv, acc);
-        }
+      for (int kk = 0; kk < T::BN / 16; ++kk) {
+        const bf16x8 sv = lds_at<bf16x8>(dsr, (qb * 32 * T::SLD + kk * 16) * 2);
+        const int o = 16 * kk * RB + 128 * (db >> 1);
+        const bf16x8 kv = cat44(tr_at(tk[0][db & 1], o), tr_at(tk[1][db & 1], o));
+        acc = mfma32(sv, kv, acc);
+      }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = qt0 + qb * 32 + acc_row(r, half);
-          if (qi < Sq)
-            unsafeAtomicAdd(a.dq_acc + ((qrow0 + qi) * a.H + head) * D + db * 32 + l32, acc[r]);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int row = qb * 32 + acc_row(r, half);
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+            acc[r], rdq, (int)((row * a.H * D + db * 32 + l32) * 4), 0, 0);
       }
     }
-  }
+    if (it + 1 < n_iter) store_stats(BUF ^ 1);
+    wait_vmem_except<16 * T::DQ_PER_WAVE>();  // the next tile's Q and dO have landed in LDS
+    __syncthreads();  // ... for every wave, and every wave is done reading dS
+  };
 
-  // Epilogue: dK (times scale) and dV, bf16, contiguous [rows_k, Hkv, D].
+  int it = 0;
+  for (; it + 1 < n_iter; it += 2) {
+    iteration(it, std::integral_constant<int, 0>{});
+    iteration(it + 1, std::integral_constant<int, 1>{});
+  }
+  if (it < n_iter) iteration(it, std::integral_constant<int, 0>{});
+
+  // Epilogue: dK (times scale) and dV as bf16 into contiguous [rows_k, Hkv, D]; rows past
+  // the sequence end are dropped by the buffer range.
   const float sc = a.scale;
+  const int64_t kv_off = ((krow0 + kb0) * a.Hkv + g) * D;
+  const uint32_t kv_bytes = (uint32_t)((krows - 1) * a.Hkv * D + D) * 2u;
+  const auto rdk = make_rsrc(reinterpret_cast<bf16*>(a.dk) + kv_off, kv_bytes);
+  const auto rdv = make_rsrc(reinterpret_cast<bf16*>(a.dv) + kv_off, kv_bytes);
 #pragma unroll
   for (int db = 0; db < T::DB; ++db) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = kb0 + wave * 32 + acc_row(r, half);
-      if (key < Sk) {
-        const int64_t off = ((krow0 + key) * a.Hkv + g) * D + db * 32 + l32;
-        reinterpret_cast<bf16*>(a.dk)[off] = (bf16)(dk[db][r] * sc);
-        reinterpret_cast<bf16*>(a.dv)[off] = (bf16)dv[db][r];
-      }
+      const int key = wave * 32 + acc_row(r, half);
+      const int off = (key * a.Hkv * D + db * 32 + l32) * 2;
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)(dk[db][r] * sc)),
+                                            rdk, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)dv[db][r]),
+                                            rdv, off, 0, 0);
     }
   }
-}
-
-template <int D>
-constexpr size_t bwd_smem_bytes() {
-  using T = BwdTile<D>;
-  return (size_t)(2 * T::Q_ELEMS + 2 * T::QT_ELEMS + T::KT_ELEMS + T::S_ELEMS) * 2 +
-         2 * T::BM * sizeof(float);
 }
 
 // ----------------------------------------------------------------------------------------

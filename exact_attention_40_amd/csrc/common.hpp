@@ -44,6 +44,25 @@ __device__ __forceinline__ bf16x8 cat44(bf16x4 lo, bf16x4 hi) {
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Buffer resource over `bytes` bytes at `base`: loads past the end return zero, so partial
+// tiles need no per-row branches (robust buffer access of the gfx9 family).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+// Transposed LDS read (ds_read_b64_tr_b16). Within each 16-lane group, if lane j points at
+// row k0 + j/4, columns n0 + 4*(j%4) .. +3 of a row-major bf16 tile, lane i receives
+// column n0 + i, rows k0 .. k0+3: an MFMA operand fragment read from the other-major layout.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<bf16*>(p)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
 // Transpose a 4-row x 8-column bf16 block held as four 16-byte rows into eight 8-byte
 // columns (column c = rows 0..3 at column c), written as 64 contiguous bytes to `dst`.
 // This builds the "key-interleaved" tile layout T[row/4][col][row%4] that lets one lane

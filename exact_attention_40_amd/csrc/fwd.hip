@@ -8,39 +8,54 @@
 // removed inside the kernel (OpenWAM PR #64, "Summary"/"Fix").
 //
 // Work decomposition (gfx950, 64-wide waves):
-//   one workgroup = 4 waves = one (unit, head, query tile of 128*QB rows);
+//   one workgroup = NW waves = one (unit, head, query tile of 32*QB*NW rows);
 //   each wave owns 32*QB query rows and keeps their Q fragments in registers;
-//   K and V tiles of 64 keys are staged through LDS, double-buffered through registers.
+//   K and V tiles of 64 keys are staged through LDS, double-buffered through registers,
+//   loaded with buffer loads that return zero past the last key (no per-row branches).
 // S^T = K Q^T is computed with 32x32x16 bf16 MFMAs so that a lane's accumulator holds one
 // query column: row statistics are per lane plus one exchange with the partner lane
 // (l ^ 32), the output rescale is a per-lane scalar, and the exponentiated scores feed
-// the O^T += V^T P^T MFMA as its B operand straight from registers. V is stored in LDS
-// as V[key/4][d][key%4] so one 8-byte read gives a lane four consecutive keys of one d.
+// the O^T += V^T P^T MFMA as its B operand straight from registers. V stays row-major in
+// LDS; its A-operand fragments (four consecutive keys of one d per lane) come from
+// transposed LDS reads.
+//
+// Rescaling: EAGER takes m_new = max(m_row, m_tile) on every tile. The lazy form keeps the
+// running max while every row's tile max exceeds it by at most kLazyTau (log2 units), so
+// exponentials are bounded by 2^kLazyTau and the accumulator is left alone; as soon as one
+// row exceeds it, every lane takes max(m_row, m_tile) before exp2 (the FlyDSL PR #1033
+// fix: a lane dragged into the rescale by the wave-wide decision gets a factor <= 1).
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "params.hpp"
 
 namespace exattn {
 
-template <int D, int QB>
+constexpr float kLazyTau = 8.f;
+
+template <int D, int NW, int QB>
 struct FwdTile {
-  static constexpr int NW = 4;
-  static constexpr int BM = NW * 32 * QB;
-  static constexpr int BN = 64;
+  static constexpr int NT = 64 * NW;         // threads per workgroup
+  static constexpr int BM = NW * 32 * QB;    // query rows per workgroup
+  static constexpr int BN = 64;              // keys per tile
   static constexpr int KB = BN / 32;
   static constexpr int DS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int KLD = D + 8;          // K row pitch (elements), breaks bank aliasing
-  static constexpr int VG = D * 4 + 8;       // pitch of one 4-key group of V
+  static constexpr int KLD = D + 8;          // K row pitch: 16 B mod 128 B, conflict-free b128
+  static constexpr int VLD = D + 16;         // V row pitch: 32 B mod 128 B, conflict-free tr reads
   static constexpr int K_ELEMS = BN * KLD;
-  static constexpr int V_ELEMS = (BN / 4) * VG;
-  static constexpr int KCH = BN * D / 8 / 256;   // 16-byte K chunks per thread
-  static constexpr int VGR = (BN / 4) * (D / 8); // 4x8 V blocks per tile
+  static constexpr int V_ELEMS = BN * VLD;
+  static constexpr int CH = BN * D / 8 / NT; // 16-byte chunks per thread, per tensor
+  static_assert(CH * NT * 8 == BN * D, "tiles must split evenly over the threads");
 };
 
-template <int D, int QB, bool CAUSAL, int MASK, bool VARLEN>
-__global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a) {
-  using T = FwdTile<D, QB>;
+template <bool B>
+using bool_c = std::integral_constant<bool, B>;
+
+template <int D, int NW, int QB, bool CAUSAL, int MASK, bool VARLEN, bool LAZY>
+__global__ void __launch_bounds__(64 * NW) fwd_kernel(FwdArgs a) {
+  using T = FwdTile<D, NW, QB>;
   __shared__ __attribute__((aligned(16))) bf16 k_lds[2 * T::K_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 v_lds[2 * T::V_ELEMS];
 
@@ -99,42 +114,48 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a) {
 
   const int kend = CAUSAL ? min(Sk, qt0 + T::BM) : Sk;
   const int ntiles = (kend + T::BN - 1) / T::BN;
+  // Leading tiles that need no masking for any row of this workgroup.
+  int n_plain = 0;
+  if (MASK == kMaskNone) {
+    int lim = Sk / T::BN;
+    if (CAUSAL) lim = min(lim, (qt0 + 1) / T::BN);
+    n_plain = min(lim, ntiles);
+  }
 
-  // Register staging of the next K/V tile.
-  u32x4 kr[T::KCH];
-  u32x4 vr[4];
-  const bool v_thread = (T::VGR >= 256) || (tid < T::VGR);
-  const int vg4 = tid / (D / 8), vd8 = tid % (D / 8);
-
+  // Per-thread 16-byte chunks of a tile: row and column are fixed, the tile base moves.
+  uint32_t k_off[T::CH], v_off[T::CH];
+  int lds_k[T::CH], lds_v[T::CH];
+#pragma unroll
+  for (int i = 0; i < T::CH; ++i) {
+    const int c = tid + i * T::NT;
+    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+    k_off[i] = (uint32_t)(row * a.k_ss + col) * 2u;
+    v_off[i] = (uint32_t)(row * a.v_ss + col) * 2u;
+    lds_k[i] = row * T::KLD + col;
+    lds_v[i] = row * T::VLD + col;
+  }
+  u32x4 kr[T::CH], vr[T::CH];
   auto load_tile = [&](int t) {
     const int kb0 = t * T::BN;
+    const int rows = min(T::BN, Sk - kb0);
+    const auto rk = make_rsrc(K + (int64_t)kb0 * a.k_ss, (uint32_t)((rows - 1) * a.k_ss + D) * 2u);
+    const auto rv = make_rsrc(V + (int64_t)kb0 * a.v_ss, (uint32_t)((rows - 1) * a.v_ss + D) * 2u);
 #pragma unroll
-    for (int i = 0; i < T::KCH; ++i) {
-      const int c = tid + i * 256;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int key = kb0 + row;
-      kr[i] = key < Sk ? ldg16(K + (int64_t)key * a.k_ss + col) : u32x4{0, 0, 0, 0};
-    }
-    if (v_thread) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb0 + 4 * vg4 + i;
-        vr[i] = key < Sk ? ldg16(V + (int64_t)key * a.v_ss + vd8 * 8) : u32x4{0, 0, 0, 0};
-      }
+    for (int i = 0; i < T::CH; ++i) {
+      kr[i] = buf_load16(rk, k_off[i]);
+      vr[i] = buf_load16(rv, v_off[i]);
     }
   };
   auto store_tile = [&](int buf) {
-    bf16* kl = k_lds + buf * T::K_ELEMS;
 #pragma unroll
-    for (int i = 0; i < T::KCH; ++i) {
-      const int c = tid + i * 256;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(kl + row * T::KLD + col) = kr[i];
+    for (int i = 0; i < T::CH; ++i) {
+      *reinterpret_cast<u32x4*>(k_lds + buf * T::K_ELEMS + lds_k[i]) = kr[i];
+      *reinterpret_cast<u32x4*>(v_lds + buf * T::V_ELEMS + lds_v[i]) = vr[i];
     }
-    if (v_thread)
-      store_4x8_transposed(v_lds + buf * T::V_ELEMS + vg4 * T::VG + vd8 * 32, vr[0], vr[1], vr[2],
-                           vr[3]);
   };
+  // Transposed-read address of this lane inside a V tile (16-lane group layout).
+  const int grp = lane >> 4, j16 = lane & 15;
+  const int v_rd = (4 * half + (j16 >> 2)) * T::VLD + 16 * (grp & 1) + 4 * (j16 & 3);
 
   f32x16 o[T::DB][QB];
   float m_run[QB], l_run[QB];
@@ -156,7 +177,27 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a) {
   const uint8_t* mask_u8 = reinterpret_cast<const uint8_t*>(a.mask);
   const bf16* mask_bf = reinterpret_cast<const bf16*>(a.mask);
 
-  for (int t = 0; t < ntiles; ++t) {
+  // Visibility of key kj for this lane's query in block qb, and its additive bias (log2).
+  auto visible = [&](int qb, int kj, float& b2) -> bool {
+    const int qi = qw0 + qb * 32 + l32;
+    bool vis = kj < Sk;
+    if (CAUSAL) vis = vis && (kj <= qi);
+    b2 = 0.f;
+    if (MASK == kMaskBool) {
+      if (vis && qi < Sq) vis = mask_u8[m_base + (int64_t)qi * a.m_si + kj] != 0;
+    }
+    if (MASK == kMaskAdd) {
+      if (vis && qi < Sq) {
+        const float bias = (float)mask_bf[m_base + (int64_t)qi * a.m_si + kj];
+        vis = bias != -INFINITY;
+        b2 = vis ? bias * kLog2e : 0.f;
+      }
+    }
+    return vis;
+  };
+
+  auto tile = [&](int t, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int buf = t & 1;
     if (t + 1 < ntiles) load_tile(t + 1);
     const bf16* kl = k_lds + buf * T::K_ELEMS;
@@ -180,55 +221,86 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a) {
     }
 
     const int kb0 = t * T::BN;
-    const bool edge = (kb0 + T::BN > Sk) || (MASK != kMaskNone) || (CAUSAL && kb0 + T::BN - 1 > qw0);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const int qi = qw0 + qb * 32 + l32;
-      float mx = -INFINITY;
+      // Tile max of the scaled scores, mt (log2 units); masked entries become -inf.
+      float mt;
+      if constexpr (!MASKED) {
+        float mx;
+        if (c2 >= 0.f) {
+          mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) {
+          for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[kb][qb][r] * c2;
-          if (edge) {
-            const int kj = kb0 + kb * 32 + acc_row(r, half);
-            bool vis = kj < Sk;
-            if (CAUSAL) vis = vis && (kj <= qi);
-            if (MASK == kMaskBool) {
-              if (vis && qi < Sq) vis = mask_u8[m_base + (int64_t)qi * a.m_si + kj] != 0;
-            }
-            if (MASK == kMaskAdd) {
-              if (vis && qi < Sq)
-                x = x + (float)mask_bf[m_base + (int64_t)qi * a.m_si + kj] * kLog2e;
-            }
-            x = vis ? x : -INFINITY;
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+          mx = fmaxf(mx, wave_xor32(mx));
+        } else {
+          mx = INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fminf(mx, s[kb][qb][r]);
+          mx = fminf(mx, wave_xor32(mx));
+        }
+        mt = mx * c2;
+      } else {
+        // Masked tile: a visible entry contributes fma(s, c2, bias2) with bias2 the
+        // additive mask in log2 units (0 otherwise), the same rounding as the plain path.
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < T::KB; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float b2;
+            const bool vis = visible(qb, kb0 + kb * 32 + acc_row(r, half), b2);
+            mx = fmaxf(mx, vis ? fmaf(s[kb][qb][r], c2, b2) : -INFINITY);
           }
-          s[kb][qb][r] = x;
-          mx = fmaxf(mx, x);
         }
+        mt = fmaxf(mx, wave_xor32(mx));
       }
-      mx = fmaxf(mx, wave_xor32(mx));
-      // Per-row max first, then exp2: exponents are never positive.
-      const float m_new = fmaxf(m_run[qb], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float corr = fast_exp2(m_run[qb] - m_use);
+      // Rescale decision, wave-uniform. Eager: whenever some row's max grows (a factor of
+      // exactly 1 elsewhere leaves those rows unchanged). Lazy: only when some row's tile
+      // max exceeds its running max by more than kLazyTau.
+      const float thr = LAZY ? kLazyTau : 0.f;
+      if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + thr) != 0) {
+        // Per-row max first, then exp2: the factor is <= 1 on every lane.
+        const float m_new = fmaxf(m_run[qb], mt);
+        const float corr = fast_exp2(m_run[qb] - ((m_new == -INFINITY) ? 0.f : m_new));
+        l_run[qb] *= corr;
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) o[db][qb] *= corr;
+        m_run[qb] = m_new;
+      }
+      const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
       float rs = 0.f;
+      if constexpr (!MASKED) {
+        const float nm = -m_use;
 #pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) {
+        for (int kb = 0; kb < T::KB; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(s[kb][qb][r] - m_use);
-          s[kb][qb][r] = p;
-          rs += p;
+          for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(fmaf(s[kb][qb][r], c2, nm));
+            s[kb][qb][r] = p;
+            rs += p;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < T::KB; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float b2;
+            const bool vis = visible(qb, kb0 + kb * 32 + acc_row(r, half), b2);
+            const float p = vis ? fast_exp2(fmaf(s[kb][qb][r], c2, b2 - m_use)) : 0.f;
+            s[kb][qb][r] = p;
+            rs += p;
+          }
         }
       }
-      l_run[qb] = l_run[qb] * corr + rs;
-      m_run[qb] = m_new;
-#pragma unroll
-      for (int db = 0; db < T::DB; ++db) o[db][qb] *= corr;
+      l_run[qb] += rs;
     }
 
-    // O^T += V^T P^T over 16-key slabs.
+    // O^T += V^T P^T over 16-key slabs; V^T fragments by transposed reads.
 #pragma unroll
     for (int kk = 0; kk < T::BN / 16; ++kk) {
       const int kb = kk >> 1, hs = (kk & 1) * 8;
@@ -239,9 +311,9 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a) {
                       s[kb][qb][hs + 4], s[kb][qb][hs + 5], s[kb][qb][hs + 6], s[kb][qb][hs + 7]);
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) {
-        const bf16* vp = vl + (4 * kk + half) * T::VG + (db * 32 + l32) * 4;
-        const bf16x8 af = cat44(*reinterpret_cast<const bf16x4*>(vp),
-                                *reinterpret_cast<const bf16x4*>(vp + 2 * T::VG));
+        // slots 0-3: keys 16kk + 4h + 0..3, slots 4-7: keys 16kk + 8 + 4h + 0..3
+        const bf16* vp = vl + (16 * kk) * T::VLD + db * 32 + v_rd;
+        const bf16x8 af = cat44(lds_read_tr4(vp), lds_read_tr4(vp + 8 * T::VLD));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma32(af, pf[qb], o[db][qb]);
       }
@@ -249,7 +321,11 @@ __global__ void __launch_bounds__(256) fwd_kernel(FwdArgs a) {
 
     if (t + 1 < ntiles) store_tile(buf ^ 1);
     __syncthreads();
-  }
+  };
+
+  int t = 0;
+  for (; t < n_plain; ++t) tile(t, bool_c<false>{});
+  for (; t < ntiles; ++t) tile(t, bool_c<true>{});
 
   // Epilogue: normalise, write out (bf16, RNE) and lse (natural log).
 #pragma unroll
@@ -290,14 +366,32 @@ __global__ void __launch_bounds__(256) fwd_tail_kernel(FwdArgs a) {
   a.lse[(int64_t)head * a.lse_row + row] = -INFINITY;
 }
 
-int fwd_block_m(int head_dim) { return FwdTile<128, 1>::BM; }
+// Variants: 0 = 8 waves x 32 rows, lazy rescale (default); 1 = 8 waves x 32 rows, eager
+// rescale; 2 = 4 waves x 64 rows, lazy; 3 = 4 waves x 32 rows, lazy. Variants 2 and 3 are
+// compiled for head_dim 128 without a mask; other problems use variant 0 or 1.
+static int g_fwd_variant = 0;
 
-template <int D, int QB>
+void set_fwd_variant(int v) { g_fwd_variant = (v >= 0 && v <= 3) ? v : 0; }
+int get_fwd_variant() { return g_fwd_variant; }
+
+static int effective_variant(int head_dim, int mask, bool varlen) {
+  const int v = g_fwd_variant;
+  if (v >= 2 && (head_dim != 128 || mask != kMaskNone || varlen)) return 0;
+  return v;
+}
+
+int fwd_block_m(int head_dim, int mask, bool varlen) {
+  const int v = effective_variant(head_dim, mask, varlen);
+  return v == 2 ? 256 : (v == 3 ? 128 : 256);
+}
+
+template <int D, int NW, int QB, bool LAZY>
 static hipError_t launch_fwd_d(const FwdArgs& a, bool causal, int mask, bool varlen, hipStream_t s) {
   const int64_t nblk = (int64_t)a.num_units * a.H * a.num_q_tiles;
   if (nblk <= 0) return hipSuccess;
-  dim3 grid((unsigned)nblk), block(256);
-#define EXATTN_FWD(C, M, V) hipLaunchKernelGGL((fwd_kernel<D, QB, C, M, V>), grid, block, 0, s, a)
+  dim3 grid((unsigned)nblk), block(64 * NW);
+#define EXATTN_FWD(C, M, V) \
+  hipLaunchKernelGGL((fwd_kernel<D, NW, QB, C, M, V, LAZY>), grid, block, 0, s, a)
   if (varlen) {
     if (causal) EXATTN_FWD(true, kMaskNone, true);
     else EXATTN_FWD(false, kMaskNone, true);
@@ -314,10 +408,29 @@ static hipError_t launch_fwd_d(const FwdArgs& a, bool causal, int mask, bool var
   return hipGetLastError();
 }
 
+template <int NW, int QB>
+static hipError_t launch_fwd_plain128(const FwdArgs& a, bool causal, hipStream_t s) {
+  const int64_t nblk = (int64_t)a.num_units * a.H * a.num_q_tiles;
+  if (nblk <= 0) return hipSuccess;
+  dim3 grid((unsigned)nblk), block(64 * NW);
+  if (causal)
+    hipLaunchKernelGGL((fwd_kernel<128, NW, QB, true, kMaskNone, false, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<128, NW, QB, false, kMaskNone, false, true>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool causal, int mask, bool varlen,
                       hipStream_t s) {
-  if (head_dim == 64) return launch_fwd_d<64, 1>(a, causal, mask, varlen, s);
-  return launch_fwd_d<128, 1>(a, causal, mask, varlen, s);
+  const int v = effective_variant(head_dim, mask, varlen);
+  if (head_dim == 64) {
+    if (v == 1) return launch_fwd_d<64, 8, 1, false>(a, causal, mask, varlen, s);
+    return launch_fwd_d<64, 8, 1, true>(a, causal, mask, varlen, s);
+  }
+  if (v == 1) return launch_fwd_d<128, 8, 1, false>(a, causal, mask, varlen, s);
+  if (v == 2) return launch_fwd_plain128<4, 2>(a, causal, s);
+  if (v == 3) return launch_fwd_plain128<4, 1>(a, causal, s);
+  return launch_fwd_d<128, 8, 1, true>(a, causal, mask, varlen, s);
 }
 
 hipError_t launch_fwd_tail(const FwdArgs& a, int head_dim, hipStream_t s) {

@@ -74,8 +74,10 @@ hipError_t launch_dq_reduce(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_kv_tail(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_zero16(void* p, int64_t bytes, hipStream_t s);  // bytes % 16 == 0
 
-// Tile shapes the host needs for grid sizing.
-int fwd_block_m(int head_dim);
+// Tile shapes the host needs for grid sizing, and the tiling selectors.
+int fwd_block_m(int head_dim, int mask, bool varlen);
+void set_fwd_variant(int v);
+int get_fwd_variant();
 int bwd_block_n(int head_dim);
 
 }  // namespace exattn

@@ -175,6 +175,17 @@ const char* exattn_last_error(void);
 exattn_status exattn_timing_enable(int enable);
 int exattn_timing_read(const char** names, double* total_ms, int* launches, int max);
 
+/*
+ * Tiling selection, for benchmarking the compiled alternatives. `kernel` 0 = forward:
+ * variant 0 (default) = 8 waves x 32 query rows per workgroup with the lazy rescale
+ * (threshold 8 in log2 units), 1 = the same tiling with an eager rescale on every tile,
+ * 2 = 4 waves x 64 rows (lazy), 3 = 4 waves x 32 rows (lazy); 2 and 3 apply to head_dim
+ * 128 without a mask or cu_seqlens, other problems fall back to 0. Every variant computes
+ * the same function up to fp32 rounding. Process-wide; not thread-safe against concurrent
+ * calls. Returns EXATTN_ERR_SHAPE for an unknown kernel or variant.
+ */
+exattn_status exattn_set_variant(int kernel, int variant);
+
 #ifdef __cplusplus
 }
 #endif

@@ -159,3 +159,10 @@ def test_timing_read_empty(lib):
     assert lib.exattn_timing_enable(1) == 0
     assert lib.exattn_timing_read(None, None, None, 0) == 0
     assert lib.exattn_timing_enable(0) == 0
+
+
+def test_set_variant(lib):
+    for v in (1, 2, 3, 0):
+        assert lib.exattn_set_variant(0, v) == 0
+    assert lib.exattn_set_variant(0, 4) == 4
+    assert lib.exattn_set_variant(7, 0) == 4
