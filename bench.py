@@ -1,10 +1,13 @@
 #!/usr/bin/env python3
 """Throughput of the attention hot path on one MI355X.
 
-One step = one forward (exattn_fwd) and one backward (exattn_bwd: delta, main backward,
-dQ reduce) over the synthetic workload B=2, S=8192, H=32 (Hkv=32), D=128, non-causal, bf16,
+One step = one forward (exattn_fwd) and one backward (exattn_bwd: delta, dK/dV kernel, dQ
+kernel) over the synthetic workload B=2, S=8192, H=32 (Hkv=32), D=128, non-causal, bf16,
 with q, k, v, dout ~ N(0,1) already resident in HBM. The FLOP count is algorithmic: 4*D
-per visible (query, key) pair for the forward and 10*D for the backward.
+per visible (query, key) pair for the forward and 10*D for the backward (five products).
+Per kernel: forward 4*D (S, PV); dK/dV kernel 8*D (S, dP, dV, dK); dQ kernel 2*D (the dQ
+product; it also recomputes S and dP, 4*D more, which is overhead of the split and not
+counted as algorithmic work).
 
 Prints one JSON line. Per-kernel durations come from HIP events the library records
 around each of its launches on the launch stream during the timed region.
@@ -28,7 +31,7 @@ METRIC = "attention fwd & bwd TFLOP/s (bf16, B2 S8192 H32 D128) + % of MFMA peak
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz (published 2.5 PFLOP/s)
 PEAK_HBM_GBS = 8000.0
 B, S, H, HKV, D = 2, 8192, 32, 32, 128
-PROFILE_PMC = os.path.join(ROOT, "profiles", "exattn_bwd_kernel_b2_s8192_h32_d128_pmc.json")
+PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash():
@@ -40,11 +43,11 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the main backward kernel from committed PMC counters,
-    or None when the kernel sources changed since they were taken."""
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from committed PMC counters, or None when the
+    kernel sources changed since they were taken."""
     try:
-        with open(PROFILE_PMC) as f:
+        with open(os.path.join(PROFILE_DIR, f"{kernel}_b2_s8192_h32_d128_pmc.json")) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -140,13 +143,25 @@ def main():
     value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
     kavg = {n: ms / cnt for n, (ms, cnt) in kern.items()}
 
-    bwd_k = kavg.get("exattn_bwd_kernel", float("nan"))
-    fwd_k = kavg.get("exattn_fwd_kernel", float("nan"))
-    achieved = bwd_flops / (bwd_k * 1e-3) / 1e12
-    traffic = measured_traffic()
+    # algorithmic and executed FLOP per launch of each matrix kernel
+    per_kernel = {
+        "exattn_fwd_kernel": (4.0 * D * pairs, 4.0 * D * pairs),
+        "exattn_bwd_dkdv_kernel": (8.0 * D * pairs, 8.0 * D * pairs),
+        "exattn_bwd_dq_kernel": (2.0 * D * pairs, 6.0 * D * pairs),
+        "exattn_bwd_fused_kernel": (10.0 * D * pairs, 10.0 * D * pairs),
+    }
+    kernels = {}
+    for name, (alg, exe) in per_kernel.items():
+        if name in kavg:
+            kernels[name] = {"ms": round(kavg[name], 4),
+                             "algorithmic_TFLOP/s": round(alg / (kavg[name] * 1e-3) / 1e12, 1),
+                             "executed_TFLOP/s": round(exe / (kavg[name] * 1e-3) / 1e12, 1)}
+    dominant = max(kernels, key=lambda n: kavg[n])
+    alg = per_kernel[dominant][0]
+    achieved = alg / (kavg[dominant] * 1e-3) / 1e12
+    traffic = measured_traffic(dominant)
     side = {}
-    for name, nbytes in (("exattn_bwd_delta_kernel", 2 * 2 * B * S * H * D + 4 * B * H * S * 3
-                          + 4 * B * S * H * D),
+    for name, nbytes in (("exattn_bwd_delta_kernel", 2 * 2 * B * S * H * D + 4 * B * H * S * 3),
                          ("exattn_bwd_dq_reduce_kernel", 4 * B * S * H * D + 2 * B * S * H * D)):
         if name in kavg:
             gbs = nbytes / (kavg[name] * 1e-3) / 1e9
@@ -176,12 +191,12 @@ def main():
         "bwd": {"ms": round(bwd_ms, 4), "TFLOP/s": round(bwd_flops / bwd_ms / 1e9, 1),
                 "frac_of_mfma_peak": round(bwd_flops / bwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4)},
         "kernels_avg_ms": {n: round(t, 4) for n, t in kavg.items()},
-        "fwd_kernel_TFLOP/s": round(fwd_flops / (fwd_k * 1e-3) / 1e12, 1),
+        "kernels": kernels,
         "side_passes": side,
-        "roofline": {"kernel": "exattn_bwd_kernel", "bound": "mfma", "achieved": round(achieved, 1),
+        "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "algorithmic_flops_per_launch": bwd_flops},
+                     "algorithmic_flops_per_launch": alg},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline()

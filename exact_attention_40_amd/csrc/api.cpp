@@ -20,9 +20,12 @@ const char* kernel_name(KernelId id) {
     case KernelId::Fwd: return "exattn_fwd_kernel";
     case KernelId::FwdTail: return "exattn_fwd_tail_kernel";
     case KernelId::Delta: return "exattn_bwd_delta_kernel";
-    case KernelId::Bwd: return "exattn_bwd_kernel";
+    case KernelId::BwdDkDv: return "exattn_bwd_dkdv_kernel";
+    case KernelId::BwdDq: return "exattn_bwd_dq_kernel";
+    case KernelId::BwdFused: return "exattn_bwd_fused_kernel";
     case KernelId::DqReduce: return "exattn_bwd_dq_reduce_kernel";
     case KernelId::KvTail: return "exattn_bwd_kv_tail_kernel";
+    case KernelId::QTail: return "exattn_bwd_q_tail_kernel";
     case KernelId::Zero: return "exattn_zero_kernel";
     default: return "unknown";
   }
@@ -172,18 +175,20 @@ Geometry geometry(const exattn_problem* p) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Workspace: [lse2 | Delta] fp32 in the lse layout, then the fp32 dQ accumulator
+// [rows_q, H, D] when the fused variant is selected.
 struct WsLayout {
-  size_t dq_acc, lse2, delta, total;
+  size_t lse2, delta, dq_acc, total;
 };
 
 WsLayout ws_layout(const exattn_problem* p) {
   const Geometry g = geometry(p);
   WsLayout w;
   const size_t nq = (size_t)g.rows_q * p->heads_q;
-  w.dq_acc = 0;
-  w.lse2 = align256(nq * p->head_dim * sizeof(float));
+  w.lse2 = 0;
   w.delta = w.lse2 + align256(nq * sizeof(float));
-  w.total = w.delta + align256(nq * sizeof(float));
+  w.dq_acc = w.delta + align256(nq * sizeof(float));
+  w.total = w.dq_acc + (get_bwd_variant() == 1 ? align256(nq * p->head_dim * sizeof(float)) : 0);
   return w;
 }
 
@@ -335,7 +340,8 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
   BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  a.dq_acc = reinterpret_cast<float*>(ws + w.dq_acc);
+  const bool fused = get_bwd_variant() == 1;
+  a.dq_acc = fused ? reinterpret_cast<float*>(ws + w.dq_acc) : nullptr;
   a.lse2 = reinterpret_cast<float*>(ws + w.lse2);
   a.delta = reinterpret_cast<float*>(ws + w.delta);
   a.q_sb = p->q_stride[0]; a.q_ss = p->q_stride[1]; a.q_sh = p->q_stride[2];
@@ -359,13 +365,18 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
   const int bn = bwd_block_n(D);
   const int maxk = g.varlen ? p->max_seqlen_k : p->seqlen_k;
   a.num_k_blocks = (maxk + bn - 1) / bn;
+  const int bmq = bwd_dq_block_m(D);
+  const int maxq = g.varlen ? p->max_seqlen_q : p->seqlen_q;
+  a.num_q_blocks = (maxq + bmq - 1) / bmq;
   a.lse_row = p->seqlen_q;
   a.rows_q = (int)g.rows_q;
   a.rows_k = (int)g.rows_k;
   a.scale = p->scale;
   a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
-  if ((int64_t)a.num_units * a.Hkv * a.num_k_blocks > INT32_MAX)
-    return fail(EXATTN_ERR_SHAPE, "too many key blocks");
+  a.rotate = fused ? 1 : 0;
+  if ((int64_t)a.num_units * a.Hkv * a.num_k_blocks > INT32_MAX ||
+      (int64_t)a.num_units * H * a.num_q_blocks > INT32_MAX)
+    return fail(EXATTN_ERR_SHAPE, "too many blocks");
 
   hipError_t e;
   if (!anyq) {
@@ -378,14 +389,24 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
   }
   e = timed(KernelId::Delta, s, [&] { return launch_delta(a, D, g.varlen, s); });
   if (e != hipSuccess) return hip_fail(e, "delta kernel launch");
+  const bool causal = p->causal != 0;
   if (a.num_k_blocks > 0) {
-    e = timed(KernelId::Bwd, s, [&] {
-      return launch_bwd(a, D, p->causal != 0, p->mask_kind, g.varlen, s);
+    e = timed(fused ? KernelId::BwdFused : KernelId::BwdDkDv, s, [&] {
+      return launch_bwd(a, D, causal, p->mask_kind, g.varlen, fused, s);
     });
     if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
   }
-  e = timed(KernelId::DqReduce, s, [&] { return launch_dq_reduce(a, D, s); });
-  if (e != hipSuccess) return hip_fail(e, "dq reduce launch");
+  if (fused) {
+    e = timed(KernelId::DqReduce, s, [&] { return launch_dq_reduce(a, D, s); });
+    if (e != hipSuccess) return hip_fail(e, "dq reduce launch");
+  } else {
+    e = timed(KernelId::BwdDq, s, [&] { return launch_bwd_dq(a, D, causal, p->mask_kind, g.varlen, s); });
+    if (e != hipSuccess) return hip_fail(e, "dq kernel launch");
+    if (g.varlen) {
+      e = timed(KernelId::QTail, s, [&] { return launch_q_tail(a, D, s); });
+      if (e != hipSuccess) return hip_fail(e, "q tail launch");
+    }
+  }
   if (g.varlen && anyk) {
     e = timed(KernelId::KvTail, s, [&] { return launch_kv_tail(a, D, s); });
     if (e != hipSuccess) return hip_fail(e, "kv tail launch");
@@ -397,6 +418,10 @@ exattn_status exattn_set_variant(int kernel, int variant) {
   g_err[0] = 0;
   if (kernel == 0 && variant >= 0 && variant <= 3) {
     set_fwd_variant(variant);
+    return EXATTN_OK;
+  }
+  if (kernel == 1 && (variant == 0 || variant == 1)) {
+    set_bwd_variant(variant);
     return EXATTN_OK;
   }
   return fail(EXATTN_ERR_SHAPE, "unknown kernel %d or variant %d", kernel, variant);

@@ -1,15 +1,17 @@
 // Backward kernels: recompute P from the stored LSE and produce dQ, dK, dV.
 //
-// Pass order on the caller's stream:
+// Pass order on the caller's stream (default, deterministic variant):
 //   1. delta_kernel    Delta_i = sum_d dO_id * O_id (fp32), lse2_i = lse_i * log2(e)
-//                      (+inf for empty rows so exp2(s - lse2) = 0), and the fp32 dQ
-//                      accumulator cleared row by row (no memset node: graph-capture safe).
+//                      (+inf for empty rows so exp2(s - lse2) = 0).
 //   2. bwd_kernel      per (unit, kv head, block of 128 keys): dK and dV accumulate in
-//                      registers over every query head of the group and every query tile;
-//                      dQ partial products go to the fp32 accumulator with atomics.
-//   3. dq_reduce       dq = bf16(dq_acc * scale).
-//   4. kv_tail_kernel  packed layouts only: key rows past cu_seqlens_k[num_seqs] get
-//                      dk = dv = 0.
+//      <DQ=false>      registers over every query head of the group and every query tile.
+//   3. bwd_dq_kernel   per (unit, head, block of 256 query rows): dQ accumulates in
+//                      registers over every key tile, recomputing S and dP.
+//   4. q_tail_kernel / kv_tail_kernel  packed layouts only: query rows past
+//                      cu_seqlens_q[num_seqs] get dq = 0, key rows past cu_seqlens_k[num_seqs]
+//                      get dk = dv = 0.
+// Fused variant: delta_kernel also clears an fp32 dQ accumulator, bwd_kernel<DQ=true> adds
+// dQ partial products into it with atomics, and dq_reduce converts it (dq = bf16(acc*scale)).
 //
 // Sources: dv = P^T dO and dk = dS^T q (flash-dmattn PR #122 "Fix NaN/Inf values in dV
 // gradients during backward pass", section "Solution", item 2); P = exp(s - lse) from the
@@ -60,9 +62,11 @@ __global__ void __launch_bounds__(256) delta_kernel(BwdArgs a) {
   for (int i = 0; i < 8; ++i) acc += (float)o[i] * (float)g[i];
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  float* dqa = a.dq_acc + r * D + sub * 8;
-  reinterpret_cast<f32x4*>(dqa)[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-  reinterpret_cast<f32x4*>(dqa)[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (a.dq_acc != nullptr) {
+    float* dqa = a.dq_acc + r * D + sub * 8;
+    reinterpret_cast<f32x4*>(dqa)[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    reinterpret_cast<f32x4*>(dqa)[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   if (sub == 0) {
     const float l = a.lse[st_idx];
     a.delta[st_idx] = acc;
@@ -73,28 +77,30 @@ __global__ void __launch_bounds__(256) delta_kernel(BwdArgs a) {
 // ----------------------------------------------------------------------------------------
 // 2. Main backward kernel.
 //
-// One workgroup = 4 waves = 128 keys of one (unit, kv head); wave w owns keys 32w..32w+31
-// and accumulates their dK and dV in fp32 (C layout: rows = keys, columns = d) across
-// every query head of the group and every query tile that can see the block. The
-// block's K and V stay in LDS for the whole loop. Per query tile of 64 rows, Q and dO are
-// copied straight from global memory into LDS (double-buffered, zero past the end), and
-// lse2/Delta through registers:
-//   S  = Q K^T and dP = dO V^T          (lane = key column, registers = query rows)
-//   P  = exp2(min(S*c + bias - lse2, 0)), dS = P * (dP - Delta); hidden entries are 0
-//   dV += P^T dO, dK += dS^T Q          (P and dS are the A operand straight from registers;
-//                                        dO and Q come from transposed LDS reads)
-//   dS -> LDS [query][key]; each wave forms 32x32 dQ tiles over the block's 128 keys
-//   (K from transposed LDS reads) and adds them to the fp32 accumulator with buffer
-//   atomics, which drop rows past the end of the sequence.
-// Row-major LDS tiles without padding use an XOR swizzle of their 16-byte chunks,
-// chunk' = chunk ^ (2*(row & 3) + ((row >> 2) & 1)), which keeps both the 16-byte row reads
-// and the 8-byte transposed reads free of bank conflicts.
+// One workgroup = 8 waves = 128 keys (four groups of 32) of one (unit, kv head), looping
+// over every query head of the group and every 64-row query tile that can see the block.
+// The waves come in pairs per key group, with two waves per SIMD:
+//   wave A (0..3): S = Q K^T, P = exp2(min(S*c + bias - lse2, 0)) (hidden entries 0),
+//                  P -> LDS (fp32), dV += P^T dO;  keeps K fragments and dV in registers;
+//   wave B (4..7): dP = dO V^T, dS = P * (dP - Delta) with P from LDS, dS -> LDS (bf16,
+//                  [query][key]), dK += dS^T Q;   keeps V fragments and dK in registers.
+// Then all eight waves form the 64 x D dQ tile from dS and the block's K (32x32 tiles, the
+// k dimension over all 128 keys) and add it to the fp32 accumulator with buffer atomics,
+// which drop rows past the end of the sequence.
+// Both roles issue their matrix products from registers (P, dS as the A operand from the C
+// layout; lane = key) and LDS (Q, dO row reads; transposed reads for the k = query
+// operands and for K in the dQ product). Q and dO tiles are copied straight from global
+// memory into swizzled LDS, double-buffered, one tile ahead; two barriers per tile.
+// Row-major LDS tiles without padding use an XOR swizzle of their 16-byte chunks (swz_f),
+// which keeps both the 16-byte row reads and the 8-byte transposed reads free of bank
+// conflicts.
 // ----------------------------------------------------------------------------------------
 template <int D>
 struct BwdTile {
-  static constexpr int NW = 4;
+  static constexpr int NW = 8;
   static constexpr int NT = 64 * NW;
   static constexpr int BN = 128;
+  static constexpr int KG = BN / 32;             // key groups (wave pairs)
   static constexpr int BM = 64;
   static constexpr int QB = BM / 32;
   static constexpr int DS = D / 16;
@@ -104,18 +110,22 @@ struct BwdTile {
   static constexpr int Q_ELEMS = BM * D;
   static constexpr int K_ELEMS = BN * D;
   static constexpr int S_ELEMS = BM * SLD;
+  static constexpr int P_BYTES = KG * QB * 4 * 64 * 16;   // fp32 P hand-over, C layout
   static constexpr int DQ_TILES = QB * DB;       // 32x32 dQ tiles per query tile
-  static constexpr int DQ_PER_WAVE = DQ_TILES / NW;
   static_assert((BM * CPR) % (64 * NW) == 0 && (BN * CPR) % (64 * NW) == 0, "even copy split");
-  static_assert(DQ_PER_WAVE * NW == DQ_TILES, "even dQ split");
+  static_assert(DQ_TILES <= NW, "one dQ tile per wave at most");
 };
 
-__device__ __forceinline__ int swz_f(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
-
-// Element offset of (row, col) in a swizzled row-major tile with D columns.
+// LDS model (64 banks of 4 bytes; 16-byte reads serve 16 lanes per cycle, 8-byte and
+// transposed reads 32 lanes per cycle). A row-major tile of 256-byte rows whose 16-byte
+// chunks are XOR-permuted by a 4x4 transpose of the row's low four bits,
+// chunk' = chunk ^ (4*(row & 3) + ((row >> 2) & 3)), is free of bank conflicts both for
+// 16-byte reads of 16 consecutive rows at one column and for transposed reads of 4
+// consecutive rows x 32 columns. Rows of D = 64 (128 bytes) keep the XOR inside 8 chunks.
 template <int D>
-__device__ __forceinline__ int swz(int row, int col) {
-  return row * D + ((((col >> 3) ^ swz_f(row))) << 3) + (col & 7);
+__device__ __forceinline__ int swz_f(int row) {
+  const int f = 4 * (row & 3) + ((row >> 2) & 3);
+  return D == 128 ? f : (f & 7);
 }
 
 // Copy R rows of D bf16 (row stride `stride` elements, rows past the buffer range read as
@@ -123,8 +133,8 @@ __device__ __forceinline__ int swz(int row, int col) {
 // fills 64 consecutive 16-byte LDS chunks, lane i the i-th, so lane i fetches the global
 // chunk that the swizzle places there. Completion is tracked by vmcnt.
 template <int D, int R, int NW>
-__device__ __forceinline__ void copy_tile_to_lds(bf16* dst, __amdgpu_buffer_rsrc_t rs, int stride,
-                                                 int wave, int lane) {
+__device__ __forceinline__ void copy_tile_to_lds(unsigned char* dst, __amdgpu_buffer_rsrc_t rs,
+                                                 int stride, int wave, int lane) {
   constexpr int CPR = D / 8;
   constexpr int ITER = R * CPR / 64 / NW;
 #pragma unroll
@@ -132,9 +142,9 @@ __device__ __forceinline__ void copy_tile_to_lds(bf16* dst, __amdgpu_buffer_rsrc
     const int p0 = (i * NW + wave) * 64;
     const int pos = p0 + lane;
     const int row = pos / CPR, pc = pos % CPR;
-    const int col = (pc ^ swz_f(row)) * 8;
+    const int col = (pc ^ swz_f<D>(row)) * 8;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (__attribute__((address_space(3))) void*)(dst + p0 * 8), 16,
+        rs, (__attribute__((address_space(3))) void*)(dst + p0 * 16), 16,
         (int)((row * stride + col) * 2), 0, 0, 0);
   }
 }
@@ -142,18 +152,20 @@ __device__ __forceinline__ void copy_tile_to_lds(bf16* dst, __amdgpu_buffer_rsrc
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Wait for every vector-memory operation except the most recent N. The counter retires in
-// issue order, so this waits for the earlier loads while the last N (the dQ atomics of the
-// current tile) stay in flight.
+// issue order, so older loads are complete while the newest N (atomics) stay in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmem_except() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int D>
+// LDS bytes: [K block | Q x2 | dO x2 | dS | P | lse2 x2 | Delta x2]; K block and dS only
+// when the kernel forms dQ.
+template <int D, bool DQ>
 constexpr size_t bwd_smem_bytes() {
   using T = BwdTile<D>;
-  return (size_t)(2 * T::K_ELEMS + 4 * T::Q_ELEMS + T::S_ELEMS) * 2 + 4 * T::BM * sizeof(float);
+  return (size_t)((DQ ? T::K_ELEMS + T::S_ELEMS : 0) + 4 * T::Q_ELEMS) * 2 + T::P_BYTES +
+         4 * T::BM * sizeof(float);
 }
 
 // LDS read at a per-lane byte address plus a compile-time byte offset (the offset folds into
@@ -166,23 +178,30 @@ __device__ __forceinline__ bf16x4 tr_at(const unsigned char* base, int imm) {
   return lds_read_tr4(reinterpret_cast<const bf16*>(base + imm));
 }
 
-template <int D, bool CAUSAL, int MASK, bool VARLEN>
-__global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
+template <int D, bool CAUSAL, int MASK, bool VARLEN, bool DQ>
+__global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
   using T = BwdTile<D>;
+  constexpr int kDqAtomics = 16;                 // buffer atomics per wave per dQ phase
   constexpr int RB = D * 2;                      // bytes per swizzled row
   constexpr int QBYTES = T::Q_ELEMS * 2;         // one Q or dO buffer
-  constexpr int KBYTES = T::K_ELEMS * 2;
+  constexpr int KBYTES = DQ ? T::K_ELEMS * 2 : 0;
+  constexpr int SBYTES = DQ ? T::S_ELEMS * 2 : 0;
   constexpr int DO_OFF = 2 * QBYTES;             // dO buffers follow the two Q buffers
-  constexpr int V_OFF = KBYTES;                  // V follows K
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  unsigned char* k_b = smem;                     // K then V
-  unsigned char* q_b = smem + 2 * KBYTES;        // Q[2] then dO[2]
-  unsigned char* ds_b = q_b + 4 * QBYTES;        // dS [BM][SLD]
-  float* lse2_l = reinterpret_cast<float*>(ds_b + T::S_ELEMS * 2);  // [2][BM]
-  float* del_l = lse2_l + 2 * T::BM;                                // [2][BM]
+  unsigned char* k_b = smem;                     // K block (dQ only)
+  unsigned char* q_b = smem + KBYTES;            // Q[2] then dO[2]
+  unsigned char* ds_b = q_b + 4 * QBYTES;        // dS [BM][SLD] bf16 (dQ only)
+  unsigned char* p_b = ds_b + SBYTES;            // P hand-over, fp32
+  float* lse2_l = reinterpret_cast<float*>(p_b + T::P_BYTES);  // [2][BM]
+  float* del_l = lse2_l + 2 * T::BM;                           // [2][BM]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The wave index is uniform across a wave; readfirstlane tells the compiler so, which keeps
+  // role branches scalar and buffer descriptors in scalar registers.
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31, grp = lane >> 4, j16 = lane & 15;
+  const bool role_a = wave < T::KG;
+  const int kg = role_a ? wave : wave - T::KG;   // key group of this wave
 
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int kbi = blk % a.num_k_blocks;
@@ -216,64 +235,63 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
   const int kb0 = kbi * T::BN;
   if (kb0 >= Sk) return;
   const int krows = min(T::BN, Sk - kb0);
-
-  // The block's K and V, row-major and swizzled, zero past the last key.
-  {
-    const bf16* K = reinterpret_cast<const bf16*>(a.k) + kb_off + (int64_t)g * a.k_sh +
-                    (int64_t)kb0 * a.k_ss;
-    const bf16* V = reinterpret_cast<const bf16*>(a.v) + vb_off + (int64_t)g * a.v_sh +
-                    (int64_t)kb0 * a.v_ss;
-    copy_tile_to_lds<D, T::BN, T::NW>(reinterpret_cast<bf16*>(k_b),
-                                     make_rsrc(K, (uint32_t)((krows - 1) * a.k_ss + D) * 2u),
-                                     (int)a.k_ss, wave, lane);
-    copy_tile_to_lds<D, T::BN, T::NW>(reinterpret_cast<bf16*>(k_b + V_OFF),
-                                     make_rsrc(V, (uint32_t)((krows - 1) * a.v_ss + D) * 2u),
-                                     (int)a.v_ss, wave, lane);
-  }
-  const int kl_w = wave * 32 + l32;          // block-local key of this lane
+  const int kl_w = kg * 32 + l32;            // block-local key of this lane
   const int kw = kb0 + kl_w;
 
-  // ---- per-lane LDS base addresses; everything else is an immediate offset ----------------
-  // Row-operand reads (row & 7 == l32 & 7 for Q/dO rows qb*32+l32 and K/V rows kl_w): the
-  // swizzle only permutes d-slab pairs within groups of four, so four bases cover all slabs.
-  const int fa_hi = l32 & 3, fa_lo = (l32 >> 2) & 1;
-  const unsigned char* aq[4];   // Q buffer 0 (+QBYTES for buffer 1, +DO_OFF for dO)
-  const unsigned char* ak[4];   // K (+V_OFF for V)
+  // The block's K (swizzled LDS, zero past the last key) and this pair's operand
+  // fragments in registers: K for wave A (S = Q K^T), V for wave B (dP = dO V^T).
+  const bf16* K = reinterpret_cast<const bf16*>(a.k) + kb_off + (int64_t)g * a.k_sh +
+                  (int64_t)kb0 * a.k_ss;
+  const bf16* V = reinterpret_cast<const bf16*>(a.v) + vb_off + (int64_t)g * a.v_sh +
+                  (int64_t)kb0 * a.v_ss;
+  const auto rk = make_rsrc(K, (uint32_t)((krows - 1) * a.k_ss + D) * 2u);
+  const auto rv = make_rsrc(V, (uint32_t)((krows - 1) * a.v_ss + D) * 2u);
+  if (DQ) copy_tile_to_lds<D, T::BN, T::NW>(k_b, rk, (int)a.k_ss, wave, lane);
+  bf16x8 kv[T::DS];
+  {
+    const auto r = role_a ? rk : rv;
+    const int st = role_a ? (int)a.k_ss : (int)a.v_ss;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int off = 32 * (i ^ fa_hi) + 16 * (half ^ fa_lo);
-    aq[i] = q_b + l32 * RB + off;
-    ak[i] = k_b + kl_w * RB + off;
+    for (int s = 0; s < T::DS; ++s)
+      kv[s] = __builtin_bit_cast(bf16x8, buf_load16(r, (uint32_t)(kl_w * st + 16 * s + 8 * half) * 2u));
   }
-  // Transposed reads of Q/dO for dV/dK: rows 16kk + 4*half + (j16>>2) (+8), columns
-  // db*32 + 16*(grp&1) + 4*(j16&3). Two bases, for db even and odd.
+
+  // ---- per-lane LDS base addresses; everything else is an immediate offset ----------------
+  // Row-operand reads of Q/dO rows qb*32 + l32, d-slab ds: one base per slab (the swizzle
+  // depends on the row's low four bits only, so qb, the buffer and Q/dO are immediates).
+  const unsigned char* aq[T::DS];   // Q buffer 0 (+QBYTES for buffer 1, +DO_OFF for dO)
+#pragma unroll
+  for (int ds = 0; ds < T::DS; ++ds)
+    aq[ds] = q_b + l32 * RB + 16 * ((2 * ds + half) ^ swz_f<D>(l32));
+  // Transposed reads of dO (wave A) or Q (wave B): rows 16kk + 4*half + (j16>>2) + 8*sec,
+  // columns db*32 + 16*(grp&1) + 4*(j16&3); one base per (db, sec), kk is an immediate.
   const int tr_row = j16 >> 2;
   const int clow = 2 * (grp & 1) + ((j16 & 3) >> 1);
-  const unsigned char* tq[2];
-  {
-    const int row = 4 * half + tr_row;
-    const int f = swz_f(row);
+  const unsigned char* tq[T::DB][2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) tq[b] = q_b + row * RB + 16 * ((4 * b + clow) ^ f) + 8 * (j16 & 1);
+  for (int sec = 0; sec < 2; ++sec) {
+    const int row = 4 * half + tr_row + 8 * sec;
+    const unsigned char* base = q_b + (role_a ? DO_OFF : 0) + row * RB + 8 * (j16 & 1);
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) tq[db][sec] = base + 16 * ((4 * db + clow) ^ swz_f<D>(row));
   }
-  // Transposed reads of K for dQ: rows 16kk + 8*half + (j16>>2) and 4 rows below.
-  const unsigned char* tk[2][2];
+  // Transposed reads of K for this wave's dQ column block: rows 16kk + 8*half + (j16>>2)
+  // and 4 rows below.
+  const int dq_db = wave % T::DB;
+  const unsigned char* tk[2];
 #pragma unroll
   for (int sec = 0; sec < 2; ++sec) {
     const int row = 8 * half + tr_row + 4 * sec;
-    const int f = swz_f(row);
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-      tk[sec][b] = k_b + row * RB + 16 * ((4 * b + clow) ^ f) + 8 * (j16 & 1);
+    tk[sec] = k_b + row * RB + 16 * ((4 * dq_db + clow) ^ swz_f<D>(row)) + 8 * (j16 & 1);
   }
-  // dS written as [query][key] from the C layout, read back as 8 consecutive keys per lane.
-  unsigned char* dsw = ds_b + (4 * half * T::SLD + kl_w) * 2;
-  const unsigned char* dsr = ds_b + (l32 * T::SLD + 8 * half) * 2;
+  unsigned char* dsw = ds_b + (4 * half * T::SLD + kl_w) * 2;         // dS write (wave B)
+  const unsigned char* dsr = ds_b + (l32 * T::SLD + 8 * half) * 2;   // dS read (dQ)
+  unsigned char* pp = p_b + kg * (T::QB * 4 * 1024) + lane * 16;    // P hand-over
   const unsigned char* st_rd = reinterpret_cast<const unsigned char*>(lse2_l) + 16 * half;
 
-  f32x16 dk[T::DB], dv[T::DB];
+  f32x16 acc[T::DB];   // dV (wave A) or dK (wave B)
 #pragma unroll
-  for (int db = 0; db < T::DB; ++db) dk[db] = dv[db] = f32x16{};
+  for (int db = 0; db < T::DB; ++db) acc[db] = f32x16{};
 
   const float c2 = a.scale_log2;
   const uint8_t* mask_u8 = reinterpret_cast<const uint8_t*>(a.mask);
@@ -284,8 +302,14 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
 
   // Staging of one query tile: Q and dO straight into LDS, lse2 and Delta via registers.
   float st_v = 0.f;
-  auto tile_head = [&](int it) { return g * a.group + it / n_qt; };
-  auto tile_q0 = [&](int it) { return qstart + (it % n_qt) * T::BM; };
+  // Workgroups of neighbouring key blocks run at the same time on one XCD; starting each
+  // at a different query tile spreads their dQ atomics over different rows.
+  const int rot = n_iter == 0 ? 0
+                : a.rotate == 1 ? (int)(((int64_t)kbi * n_iter) / a.num_k_blocks) % n_iter
+                : a.rotate == 2 ? (kbi & 7) % n_iter : 0;
+  auto tile_t = [&](int it) { int t = it + rot; return t >= n_iter ? t - n_iter : t; };
+  auto tile_head = [&](int it) { return g * a.group + tile_t(it) / n_qt; };
+  auto tile_q0 = [&](int it) { return qstart + (tile_t(it) % n_qt) * T::BM; };
   auto load_q = [&](int it, int buf) {
     const int head = tile_head(it), qt0 = tile_q0(it);
     const int rows = min(T::BM, Sq - qt0);
@@ -293,10 +317,10 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
                      (int64_t)qt0 * a.q_ss;
     const bf16* Dp = reinterpret_cast<const bf16*>(a.dout) + dob_off + (int64_t)head * a.do_sh +
                      (int64_t)qt0 * a.do_ss;
-    copy_tile_to_lds<D, T::BM, T::NW>(reinterpret_cast<bf16*>(q_b + buf * QBYTES),
+    copy_tile_to_lds<D, T::BM, T::NW>(q_b + buf * QBYTES,
                                      make_rsrc(Qp, (uint32_t)((rows - 1) * a.q_ss + D) * 2u),
                                      (int)a.q_ss, wave, lane);
-    copy_tile_to_lds<D, T::BM, T::NW>(reinterpret_cast<bf16*>(q_b + DO_OFF + buf * QBYTES),
+    copy_tile_to_lds<D, T::BM, T::NW>(q_b + DO_OFF + buf * QBYTES,
                                      make_rsrc(Dp, (uint32_t)((rows - 1) * a.do_ss + D) * 2u),
                                      (int)a.do_ss, wave, lane);
     const int64_t st = VARLEN ? (int64_t)head * a.lse_row + st_unit
@@ -312,9 +336,16 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
     else if (tid < 2 * T::BM) del_l[buf * T::BM + tid - T::BM] = st_v;
   };
 
+  // Prefetch distance two: tiles 0 and 1 now; tile it + 2 is requested during the dQ phase
+  // of tile it, before that phase's atomics, so waiting for it never waits for atomics.
   if (n_iter > 0) {
     load_q(0, 0);
     store_stats(0);
+  }
+  if (n_iter > 1) {
+    wait_vmem();
+    load_q(1, 1);
+    store_stats(1);
   }
   wait_vmem();
   __syncthreads();
@@ -323,26 +354,22 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
   auto iteration = [&](int it, auto buf_tag) {
     constexpr int BUF = decltype(buf_tag)::value;
     constexpr int QO = BUF * QBYTES;
-    if (it + 1 < n_iter) load_q(it + 1, BUF ^ 1);
     const int head = tile_head(it), qt0 = tile_q0(it);
     const bool edge = (kb0 + T::BN > Sk) || (qt0 + T::BM > Sq) || (MASK != kMaskNone) ||
                       (CAUSAL && kb0 + T::BN - 1 > qt0);
     const int64_t m_base = (int64_t)unit * a.m_sb + (int64_t)head * a.m_sh;
 
-    // P = exp2(min(S*c + bias - lse2, 0)) and dS = P * (dP - Delta), in place.
-    auto softmax_grad = [&](f32x16& s, f32x16& dp, int qb, auto edge_tag) {
+    // P = exp2(min(S*c + bias - lse2, 0)) in place (wave A).
+    auto softmax_p = [&](f32x16& s, int qb, auto edge_tag) {
       constexpr bool EDGE = decltype(edge_tag)::value;
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const int soff = BUF * T::BM * 4 + (qb * 32 + 8 * rg) * 4;
-        const f32x4 l2 = lds_at<f32x4>(st_rd, soff);
-        const f32x4 dd = lds_at<f32x4>(st_rd, soff + 2 * T::BM * 4);
+        const f32x4 l2 = lds_at<f32x4>(st_rd, BUF * T::BM * 4 + (qb * 32 + 8 * rg) * 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rg + e;
-          float p;
           if constexpr (!EDGE) {
-            p = fast_exp2(fminf(fmaf(s[r], c2, -l2[e]), 0.f));
+            s[r] = fast_exp2(fminf(fmaf(s[r], c2, -l2[e]), 0.f));
           } else {
             // Branch-free visibility: mask reads use indices clamped into range.
             const int qi = qt0 + qb * 32 + 8 * rg + 4 * half + e;
@@ -360,79 +387,99 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
               }
             }
             const float e2 = fast_exp2(fminf(fmaf(s[r], c2, b2 - l2[e]), 0.f));
-            p = vis ? e2 : 0.f;
+            s[r] = vis ? e2 : 0.f;
           }
-          s[r] = p;
-          dp[r] = p * (dp[r] - dd[e]);
         }
       }
     };
 
+    // ---- phase 1: S and P (A) / dP (B) ----
+    f32x16 sp[T::QB];
 #pragma unroll
-    for (int qb = 0; qb < T::QB; ++qb) {
-      // S = Q K^T and dP = dO V^T for 32 query rows: rows = queries, columns = keys.
-      f32x16 s = f32x16{}, dp = f32x16{};
+    for (int qb = 0; qb < T::QB; ++qb) sp[qb] = f32x16{};
+    {
+      const int po = role_a ? 0 : DO_OFF;    // A multiplies Q by K, B multiplies dO by V
 #pragma unroll
       for (int ds = 0; ds < T::DS; ++ds) {
-        const int i = ds & 3, m = (ds >> 2) * 128;
-        const bf16x8 kf = lds_at<bf16x8>(ak[i], m);
-        const bf16x8 vf = lds_at<bf16x8>(ak[i], m + V_OFF);
-        s = mfma32(lds_at<bf16x8>(aq[i], QO + qb * 32 * RB + m), kf, s);
-        dp = mfma32(lds_at<bf16x8>(aq[i], DO_OFF + QO + qb * 32 * RB + m), vf, dp);
+#pragma unroll
+        for (int qb = 0; qb < T::QB; ++qb)
+          sp[qb] = mfma32(lds_at<bf16x8>(aq[ds] + po, QO + qb * 32 * RB), kv[ds], sp[qb]);
       }
-      if (edge) softmax_grad(s, dp, qb, bool_c<true>{});
-      else softmax_grad(s, dp, qb, bool_c<false>{});
-      // dV += P^T dO and dK += dS^T Q over the two 16-row slabs of these 32 rows.
+    }
+    if (role_a) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int kk = 2 * qb + ks, hs = ks * 8;
-        const bf16x8 pa = cvt8(s[hs + 0], s[hs + 1], s[hs + 2], s[hs + 3], s[hs + 4], s[hs + 5],
-                               s[hs + 6], s[hs + 7]);
-        const bf16x8 sa = cvt8(dp[hs + 0], dp[hs + 1], dp[hs + 2], dp[hs + 3], dp[hs + 4],
-                               dp[hs + 5], dp[hs + 6], dp[hs + 7]);
+      for (int qb = 0; qb < T::QB; ++qb) {
+        if (edge) softmax_p(sp[qb], qb, bool_c<true>{});
+        else softmax_p(sp[qb], qb, bool_c<false>{});
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db) {
-          const unsigned char* tb = tq[db & 1];
-          const int o = QO + 16 * kk * RB + 128 * (db >> 1);
-          const bf16x8 ob = cat44(tr_at(tb, DO_OFF + o), tr_at(tb, DO_OFF + o + 8 * RB));
-          const bf16x8 qv = cat44(tr_at(tb, o), tr_at(tb, o + 8 * RB));
-          dv[db] = mfma32(pa, ob, dv[db]);
-          dk[db] = mfma32(sa, qv, dk[db]);
+        for (int rg = 0; rg < 4; ++rg)
+          *reinterpret_cast<f32x4*>(pp + (qb * 4 + rg) * 1024) =
+              f32x4{sp[qb][4 * rg], sp[qb][4 * rg + 1], sp[qb][4 * rg + 2], sp[qb][4 * rg + 3]};
+      }
+    }
+    __syncthreads();  // P visible to wave B
+
+    // ---- phase 2: dV += P^T dO (A) / dS, dK += dS^T Q (B) ----
+    if (!role_a) {
+#pragma unroll
+      for (int qb = 0; qb < T::QB; ++qb) {
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const f32x4 pv = *reinterpret_cast<const f32x4*>(pp + (qb * 4 + rg) * 1024);
+          const f32x4 dd =
+              lds_at<f32x4>(st_rd, 2 * T::BM * 4 + BUF * T::BM * 4 + (qb * 32 + 8 * rg) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sp[qb][4 * rg + e] = pv[e] * (sp[qb][4 * rg + e] - dd[e]);
+        }
+        if (DQ) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            *reinterpret_cast<bf16*>(dsw + (qb * 32 + 8 * (r >> 2) + (r & 3)) * T::SLD * 2) =
+                (bf16)sp[qb][r];
         }
       }
-      // dS -> LDS as [query][key] for the dQ product.
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        *reinterpret_cast<bf16*>(dsw + (qb * 32 + 8 * (r >> 2) + (r & 3)) * T::SLD * 2) = (bf16)dp[r];
     }
-    __syncthreads();  // dS complete; every wave is done with this tile's Q and dO
-
-    // dQ tiles: rows = queries, columns = d; k = the block's 128 keys.
-    const int qrows = min(T::BM, Sq - qt0);
-    float* dqp = a.dq_acc + ((qrow0 + qt0) * a.H + head) * D;
-    const auto rdq = make_rsrc(dqp, (uint32_t)((qrows - 1) * a.H * D + D) * 4u);
 #pragma unroll
-    for (int tt = 0; tt < T::DQ_PER_WAVE; ++tt) {
-      const int tile = wave * T::DQ_PER_WAVE + tt;
-      const int qb = tile / T::DB, db = tile % T::DB;
-      f32x16 acc = f32x16{};
+    for (int kk = 0; kk < T::BM / 16; ++kk) {
+      const int qb = kk >> 1, hs = (kk & 1) * 8;
+      const bf16x8 pa = cvt8(sp[qb][hs + 0], sp[qb][hs + 1], sp[qb][hs + 2], sp[qb][hs + 3],
+                             sp[qb][hs + 4], sp[qb][hs + 5], sp[qb][hs + 6], sp[qb][hs + 7]);
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
+        const int o = QO + 16 * kk * RB;
+        const bf16x8 bv = cat44(tr_at(tq[db][0], o), tr_at(tq[db][1], o));
+        acc[db] = mfma32(pa, bv, acc[db]);
+      }
+    }
+    // Tile it + 1 was requested during the previous dQ phase; only the newest memory
+    // operations (that phase's atomics) may still be in flight.
+    if (DQ && wave < T::DQ_TILES) wait_vmem_except<kDqAtomics>();
+    else wait_vmem();
+    if (it >= 1 && it + 1 < n_iter) store_stats(BUF ^ 1);
+    __syncthreads();  // dS complete; next tile's staging visible; P consumed
+
+    // ---- phase 3: request tile it + 2, then the dQ tile of this wave over 128 keys ----
+    if (it + 2 < n_iter) load_q(it + 2, BUF);
+    if (DQ && wave < T::DQ_TILES) {
+      const int qb = wave / T::DB, db = dq_db;
+      const int qrows = min(T::BM, Sq - qt0);
+      float* dqp = a.dq_acc + ((qrow0 + qt0) * a.H + head) * D;
+      const auto rdq = make_rsrc(dqp, (uint32_t)((qrows - 1) * a.H * D + D) * 4u);
+      f32x16 dq = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < T::BN / 16; ++kk) {
         const bf16x8 sv = lds_at<bf16x8>(dsr, (qb * 32 * T::SLD + kk * 16) * 2);
-        const int o = 16 * kk * RB + 128 * (db >> 1);
-        const bf16x8 kv = cat44(tr_at(tk[0][db & 1], o), tr_at(tk[1][db & 1], o));
-        acc = mfma32(sv, kv, acc);
+        const int o = 16 * kk * RB;
+        const bf16x8 kvv = cat44(tr_at(tk[0], o), tr_at(tk[1], o));
+        dq = mfma32(sv, kvv, dq);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = qb * 32 + acc_row(r, half);
         __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
-            acc[r], rdq, (int)((row * a.H * D + db * 32 + l32) * 4), 0, 0);
+            dq[r], rdq, (int)((row * a.H * D + db * 32 + l32) * 4), 0, 0);
       }
     }
-    if (it + 1 < n_iter) store_stats(BUF ^ 1);
-    wait_vmem_except<16 * T::DQ_PER_WAVE>();  // the next tile's Q and dO have landed in LDS
-    __syncthreads();  // ... for every wave, and every wave is done reading dS
   };
 
   int it = 0;
@@ -442,23 +489,255 @@ __global__ void __launch_bounds__(256) bwd_kernel(BwdArgs a) {
   }
   if (it < n_iter) iteration(it, std::integral_constant<int, 0>{});
 
-  // Epilogue: dK (times scale) and dV as bf16 into contiguous [rows_k, Hkv, D]; rows past
-  // the sequence end are dropped by the buffer range.
-  const float sc = a.scale;
+  // Epilogue: dV (wave A) or dK times scale (wave B) as bf16 into contiguous
+  // [rows_k, Hkv, D]; rows past the sequence end are dropped by the buffer range.
+  const float sc = role_a ? 1.f : a.scale;
   const int64_t kv_off = ((krow0 + kb0) * a.Hkv + g) * D;
   const uint32_t kv_bytes = (uint32_t)((krows - 1) * a.Hkv * D + D) * 2u;
-  const auto rdk = make_rsrc(reinterpret_cast<bf16*>(a.dk) + kv_off, kv_bytes);
-  const auto rdv = make_rsrc(reinterpret_cast<bf16*>(a.dv) + kv_off, kv_bytes);
+  const auto rout = make_rsrc(reinterpret_cast<bf16*>(role_a ? a.dv : a.dk) + kv_off, kv_bytes);
 #pragma unroll
   for (int db = 0; db < T::DB; ++db) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = wave * 32 + acc_row(r, half);
+      const int key = kg * 32 + acc_row(r, half);
       const int off = (key * a.Hkv * D + db * 32 + l32) * 2;
-      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)(dk[db][r] * sc)),
-                                            rdk, off, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)dv[db][r]),
-                                            rdv, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)(acc[db][r] * sc)),
+                                            rout, off, 0, 0);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// 2b. dQ kernel (deterministic, no atomics).
+//
+// One workgroup = 8 waves = 256 query rows of one (unit, head); each wave owns 32 rows and
+// keeps their Q and dO fragments (B operand: column = query, k-slots = d) and their lse2
+// and Delta (one per lane) in registers. Key tiles of 64 (K and V, row-major, swizzled) are
+// copied straight into LDS, double-buffered. Per tile:
+//   S^T = K Q^T and dP^T = V dO^T        (lane = query column, registers = keys)
+//   P = exp2(min(S*c + bias - lse2, 0)), dS = P * (dP - Delta); hidden entries are 0
+//   dQ^T += K^T dS^T                     (K^T fragments by transposed LDS reads; dS^T is the
+//                                          B operand straight from registers)
+// dQ accumulates over every key tile in registers and is written once, times the scale, as
+// bf16: the sum order is fixed, so dQ is bitwise reproducible.
+// ----------------------------------------------------------------------------------------
+template <int D>
+struct DqTile {
+  static constexpr int NW = 8;
+  static constexpr int BM = NW * 32;
+  static constexpr int BN = 64;
+  static constexpr int KB = BN / 32;
+  static constexpr int DS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int TBYTES = BN * D * 2;      // one K or V tile
+  static_assert((BN * D / 8) % (64 * NW) == 0, "even copy split");
+};
+
+template <int D, bool CAUSAL, int MASK, bool VARLEN>
+__global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
+  using T = DqTile<D>;
+  constexpr int RB = D * 2;
+  constexpr int V_OFF = 2 * T::TBYTES;           // V buffers follow the two K buffers
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * T::TBYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, l32 = lane & 31, grp = lane >> 4, j16 = lane & 15;
+
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int n_qtiles = a.num_q_blocks;
+  int qtile = blk % n_qtiles;
+  const int uh = blk / n_qtiles;
+  const int head = uh % a.H, unit = uh / a.H, g = head / a.group;
+  if (CAUSAL) qtile = n_qtiles - 1 - qtile;      // longest rows first
+
+  int Sq, Sk;
+  int64_t qrow0, q_base, k_base, v_base, do_base, st_base, m_base = 0;
+  if constexpr (VARLEN) {
+    const int qs = a.cu_q[unit], ks = a.cu_k[unit];
+    Sq = a.cu_q[unit + 1] - qs;
+    Sk = a.cu_k[unit + 1] - ks;
+    qrow0 = qs;
+    q_base = (int64_t)qs * a.q_ss + (int64_t)head * a.q_sh;
+    do_base = (int64_t)qs * a.do_ss + (int64_t)head * a.do_sh;
+    k_base = (int64_t)ks * a.k_ss + (int64_t)g * a.k_sh;
+    v_base = (int64_t)ks * a.v_ss + (int64_t)g * a.v_sh;
+    st_base = (int64_t)head * a.lse_row + qs;
+  } else {
+    Sq = a.Sq;
+    Sk = a.Sk;
+    qrow0 = (int64_t)unit * a.Sq;
+    q_base = (int64_t)unit * a.q_sb + (int64_t)head * a.q_sh;
+    do_base = (int64_t)unit * a.do_sb + (int64_t)head * a.do_sh;
+    k_base = (int64_t)unit * a.k_sb + (int64_t)g * a.k_sh;
+    v_base = (int64_t)unit * a.v_sb + (int64_t)g * a.v_sh;
+    st_base = ((int64_t)unit * a.H + head) * a.Sq;
+    m_base = (int64_t)unit * a.m_sb + (int64_t)head * a.m_sh;
+  }
+  const int qt0 = qtile * T::BM;
+  if (qt0 >= Sq) return;
+  const bf16* K = reinterpret_cast<const bf16*>(a.k) + k_base;
+  const bf16* V = reinterpret_cast<const bf16*>(a.v) + v_base;
+
+  // This lane's query row: Q and dO fragments, lse2 and Delta (zero / +inf past the end).
+  const int qw0 = qt0 + wave * 32;
+  const int qi = qw0 + l32;
+  bf16x8 qf[T::DS], df[T::DS];
+  float l2 = INFINITY, dl = 0.f;
+  if (qi < Sq) {
+    const bf16* qr = reinterpret_cast<const bf16*>(a.q) + q_base + (int64_t)qi * a.q_ss + 8 * half;
+    const bf16* dr = reinterpret_cast<const bf16*>(a.dout) + do_base + (int64_t)qi * a.do_ss + 8 * half;
+#pragma unroll
+    for (int s = 0; s < T::DS; ++s) {
+      qf[s] = *reinterpret_cast<const bf16x8*>(qr + 16 * s);
+      df[s] = *reinterpret_cast<const bf16x8*>(dr + 16 * s);
+    }
+    l2 = a.lse2[st_base + qi];
+    dl = a.delta[st_base + qi];
+  } else {
+#pragma unroll
+    for (int s = 0; s < T::DS; ++s) qf[s] = df[s] = bf16x8{};
+  }
+
+  const int kend = CAUSAL ? min(Sk, qt0 + T::BM) : Sk;
+  const int ntiles = (kend + T::BN - 1) / T::BN;
+  int n_plain = 0;
+  if (MASK == kMaskNone) {
+    int lim = Sk / T::BN;
+    if (CAUSAL) lim = min(lim, (qt0 + 1) / T::BN);
+    n_plain = min(lim, ntiles);
+  }
+
+  auto load_tile = [&](int t, int buf) {
+    const int kb0 = t * T::BN;
+    const int rows = min(T::BN, Sk - kb0);
+    copy_tile_to_lds<D, T::BN, T::NW>(smem + buf * T::TBYTES,
+                                     make_rsrc(K + (int64_t)kb0 * a.k_ss, (uint32_t)((rows - 1) * a.k_ss + D) * 2u),
+                                     (int)a.k_ss, wave, lane);
+    copy_tile_to_lds<D, T::BN, T::NW>(smem + V_OFF + buf * T::TBYTES,
+                                     make_rsrc(V + (int64_t)kb0 * a.v_ss, (uint32_t)((rows - 1) * a.v_ss + D) * 2u),
+                                     (int)a.v_ss, wave, lane);
+  };
+
+  // Per-lane LDS bases: row reads (keys kb*32 + l32, slab ds) and transposed K reads (keys
+  // 16kk + 4*half + (j16>>2) + 8*sec, d = db*32 + 16*(grp&1) + 4*(j16&3)).
+  const unsigned char* ar[T::DS];
+#pragma unroll
+  for (int ds = 0; ds < T::DS; ++ds) ar[ds] = smem + l32 * RB + 16 * ((2 * ds + half) ^ swz_f<D>(l32));
+  const int clow = 2 * (grp & 1) + ((j16 & 3) >> 1);
+  const unsigned char* tk[T::DB][2];
+#pragma unroll
+  for (int sec = 0; sec < 2; ++sec) {
+    const int row = 4 * half + (j16 >> 2) + 8 * sec;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+      tk[db][sec] = smem + row * RB + 16 * ((4 * db + clow) ^ swz_f<D>(row)) + 8 * (j16 & 1);
+  }
+
+  f32x16 dq[T::DB];
+#pragma unroll
+  for (int db = 0; db < T::DB; ++db) dq[db] = f32x16{};
+
+  if (ntiles > 0) load_tile(0, 0);
+  wait_vmem();
+  __syncthreads();
+
+  const float c2 = a.scale_log2;
+  const uint8_t* mask_u8 = reinterpret_cast<const uint8_t*>(a.mask);
+  const bf16* mask_bf = reinterpret_cast<const bf16*>(a.mask);
+
+  auto tile = [&](int t, auto buf_tag, auto masked_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr int KO = BUF * T::TBYTES;
+    if (t + 1 < ntiles) load_tile(t + 1, BUF ^ 1);
+    f32x16 s[T::KB], dp[T::KB];
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb) s[kb] = dp[kb] = f32x16{};
+#pragma unroll
+    for (int ds = 0; ds < T::DS; ++ds) {
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb) {
+        s[kb] = mfma32(lds_at<bf16x8>(ar[ds], KO + kb * 32 * RB), qf[ds], s[kb]);
+        dp[kb] = mfma32(lds_at<bf16x8>(ar[ds], V_OFF + KO + kb * 32 * RB), df[ds], dp[kb]);
+      }
+    }
+    const int kb0 = t * T::BN;
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p;
+        if constexpr (!MASKED) {
+          p = fast_exp2(fminf(fmaf(s[kb][r], c2, -l2), 0.f));
+        } else {
+          const int kj = kb0 + kb * 32 + acc_row(r, half);
+          bool vis = (kj < Sk) && (qi < Sq);
+          if (CAUSAL) vis = vis && (kj <= qi);
+          float b2 = 0.f;
+          if (MASK != kMaskNone) {
+            const int64_t mi = m_base + (int64_t)min(qi, Sq - 1) * a.m_si + min(kj, Sk - 1);
+            if (MASK == kMaskBool) {
+              vis = vis && (mask_u8[mi] != 0);
+            } else {
+              const float bias = (float)mask_bf[mi];
+              vis = vis && (bias != -INFINITY);
+              b2 = vis ? bias * kLog2e : 0.f;
+            }
+          }
+          const float e2 = fast_exp2(fminf(fmaf(s[kb][r], c2, b2 - l2), 0.f));
+          p = vis ? e2 : 0.f;
+        }
+        dp[kb][r] = p * (dp[kb][r] - dl);
+      }
+    }
+    // dQ^T += K^T dS^T over 16-key slabs.
+#pragma unroll
+    for (int kk = 0; kk < T::BN / 16; ++kk) {
+      const int kb = kk >> 1, hs = (kk & 1) * 8;
+      const bf16x8 sb = cvt8(dp[kb][hs + 0], dp[kb][hs + 1], dp[kb][hs + 2], dp[kb][hs + 3],
+                             dp[kb][hs + 4], dp[kb][hs + 5], dp[kb][hs + 6], dp[kb][hs + 7]);
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
+        const int o = KO + 16 * kk * RB;
+        const bf16x8 ka = cat44(tr_at(tk[db][0], o), tr_at(tk[db][1], o));
+        dq[db] = mfma32(ka, sb, dq[db]);
+      }
+    }
+    wait_vmem();      // the next tile has landed in LDS
+    __syncthreads();  // ... for every wave, and every wave is done with this one
+  };
+
+  int t = 0;
+  for (; t + 1 < n_plain; t += 2) {
+    tile(t, std::integral_constant<int, 0>{}, bool_c<false>{});
+    tile(t + 1, std::integral_constant<int, 1>{}, bool_c<false>{});
+  }
+  // Remaining tiles (odd plain tile, masked tiles) with a run-time buffer parity.
+  for (; t < ntiles; ++t) {
+    const bool plain = t < n_plain;
+    if ((t & 1) == 0) {
+      if (plain) tile(t, std::integral_constant<int, 0>{}, bool_c<false>{});
+      else tile(t, std::integral_constant<int, 0>{}, bool_c<true>{});
+    } else {
+      if (plain) tile(t, std::integral_constant<int, 1>{}, bool_c<false>{});
+      else tile(t, std::integral_constant<int, 1>{}, bool_c<true>{});
+    }
+  }
+
+  // Epilogue: dq = bf16(dQ * scale), dense [rows_q, H, D]; rows past Sq are not written.
+  if (qi < Sq) {
+    bf16* row = reinterpret_cast<bf16*>(a.dq) + ((qrow0 + qi) * a.H + head) * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d = db * 32 + 8 * rg + 4 * half;
+        f32x4 vv = {dq[db][4 * rg] * sc, dq[db][4 * rg + 1] * sc, dq[db][4 * rg + 2] * sc,
+                    dq[db][4 * rg + 3] * sc};
+        *reinterpret_cast<bf16x4*>(row + d) = __builtin_convertvector(vv, bf16x4);
+      }
     }
   }
 }
@@ -488,6 +767,15 @@ __global__ void __launch_bounds__(256) kv_tail_kernel(BwdArgs a, int64_t row_chu
   reinterpret_cast<u32x4*>(a.dv)[i] = u32x4{0, 0, 0, 0};
 }
 
+// Packed layouts, deterministic dQ: query rows past cu_seqlens_q[num_seqs] get dq = 0.
+__global__ void __launch_bounds__(256) q_tail_kernel(BwdArgs a, int64_t row_chunks, int chunks_per_row) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= row_chunks) return;
+  const int64_t row = i / chunks_per_row;
+  if (row < a.cu_q[a.num_units]) return;
+  reinterpret_cast<u32x4*>(a.dq)[i] = u32x4{0, 0, 0, 0};
+}
+
 // Zero-fill of a buffer, 16 bytes per thread (used instead of a memset node so that the
 // call stays capturable into a graph).
 __global__ void __launch_bounds__(256) zero16_kernel(u32x4* p, int64_t n16) {
@@ -508,6 +796,12 @@ hipError_t launch_zero16(void* p, int64_t bytes, hipStream_t s) {
 
 int bwd_block_n(int head_dim) { return BwdTile<128>::BN; }
 
+// Backward variants: 0 = dK/dV kernel + separate dQ kernel (deterministic), 1 = one fused
+// kernel with fp32 dQ atomics.
+static int g_bwd_variant = 0;
+void set_bwd_variant(int v) { g_bwd_variant = (v == 1) ? 1 : 0; }
+int get_bwd_variant() { return g_bwd_variant; }
+
 hipError_t launch_delta(const BwdArgs& a, int head_dim, bool varlen, hipStream_t s) {
   const int64_t nrows = (int64_t)a.rows_q * a.H;
   if (nrows <= 0) return hipSuccess;
@@ -524,16 +818,17 @@ hipError_t launch_delta(const BwdArgs& a, int head_dim, bool varlen, hipStream_t
 }
 
 template <int D>
-static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, int mask, bool varlen, hipStream_t s) {
+static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, int mask, bool varlen, bool fused,
+                               hipStream_t s) {
   const int64_t nblk = (int64_t)a.num_units * a.Hkv * a.num_k_blocks;
   if (nblk <= 0) return hipSuccess;
-  constexpr size_t smem = bwd_smem_bytes<D>();
-  dim3 grid((unsigned)nblk), block(256);
+  dim3 grid((unsigned)nblk), block(512);
 #define EXATTN_BWD(C, M, V)                                                                    \
   do {                                                                                         \
-    auto kfn = bwd_kernel<D, C, M, V>;                                                         \
+    auto kfn = fused ? bwd_kernel<D, C, M, V, true> : bwd_kernel<D, C, M, V, false>;           \
+    const int smem = (int)(fused ? bwd_smem_bytes<D, true>() : bwd_smem_bytes<D, false>());   \
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                     \
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem); \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);      \
     if (e != hipSuccess) return e;                                                             \
     hipLaunchKernelGGL(kfn, grid, block, smem, s, a);                                          \
   } while (0)
@@ -554,16 +849,56 @@ static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, int mask, bool var
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool causal, int mask, bool varlen,
-                      hipStream_t s) {
-  if (head_dim == 64) return launch_bwd_d<64>(a, causal, mask, varlen, s);
-  return launch_bwd_d<128>(a, causal, mask, varlen, s);
+                      bool fused, hipStream_t s) {
+  if (head_dim == 64) return launch_bwd_d<64>(a, causal, mask, varlen, fused, s);
+  return launch_bwd_d<128>(a, causal, mask, varlen, fused, s);
 }
+
+template <int D>
+static hipError_t launch_bwd_dq_d(const BwdArgs& a, bool causal, int mask, bool varlen,
+                                  hipStream_t s) {
+  const int64_t nblk = (int64_t)a.num_units * a.H * a.num_q_blocks;
+  if (nblk <= 0) return hipSuccess;
+  dim3 grid((unsigned)nblk), block(512);
+#define EXATTN_DQ(C, M, V) hipLaunchKernelGGL((bwd_dq_kernel<D, C, M, V>), grid, block, 0, s, a)
+  if (varlen) {
+    if (causal) EXATTN_DQ(true, kMaskNone, true);
+    else EXATTN_DQ(false, kMaskNone, true);
+  } else if (causal) {
+    if (mask == kMaskBool) EXATTN_DQ(true, kMaskBool, false);
+    else if (mask == kMaskAdd) EXATTN_DQ(true, kMaskAdd, false);
+    else EXATTN_DQ(true, kMaskNone, false);
+  } else {
+    if (mask == kMaskBool) EXATTN_DQ(false, kMaskBool, false);
+    else if (mask == kMaskAdd) EXATTN_DQ(false, kMaskAdd, false);
+    else EXATTN_DQ(false, kMaskNone, false);
+  }
+#undef EXATTN_DQ
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, bool causal, int mask, bool varlen,
+                         hipStream_t s) {
+  if (head_dim == 64) return launch_bwd_dq_d<64>(a, causal, mask, varlen, s);
+  return launch_bwd_dq_d<128>(a, causal, mask, varlen, s);
+}
+
+int bwd_dq_block_m(int head_dim) { return DqTile<128>::BM; }
 
 hipError_t launch_dq_reduce(const BwdArgs& a, int head_dim, hipStream_t s) {
   const int64_t n8 = (int64_t)a.rows_q * a.H * head_dim / 8;
   if (n8 <= 0) return hipSuccess;
   dim3 grid((unsigned)((n8 + 255) / 256)), block(256);
   hipLaunchKernelGGL(dq_reduce_kernel, grid, block, 0, s, a, n8);
+  return hipGetLastError();
+}
+
+hipError_t launch_q_tail(const BwdArgs& a, int head_dim, hipStream_t s) {
+  const int cpr = a.H * head_dim / 8;
+  const int64_t n = (int64_t)a.rows_q * cpr;
+  if (n <= 0) return hipSuccess;
+  dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  hipLaunchKernelGGL(q_tail_kernel, grid, block, 0, s, a, n, cpr);
   return hipGetLastError();
 }
 

@@ -59,7 +59,8 @@ __global__ void __launch_bounds__(64 * NW) fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 k_lds[2 * T::K_ELEMS];
   __shared__ __attribute__((aligned(16))) bf16 v_lds[2 * T::V_ELEMS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform across the wave
   const int half = lane >> 5, l32 = lane & 31;
 
   const int blk = xcd_remap(blockIdx.x, gridDim.x);

@@ -37,7 +37,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;     // fp32 [rows_q, H, D]
+  float* dq_acc;     // fp32 [rows_q, H, D], fused variant only (else NULL)
   float* lse2;       // fp32, lse layout: lse * log2(e), +inf for empty rows
   float* delta;      // fp32, lse layout: rowsum(dout * out)
   int64_t q_sb, q_ss, q_sh;
@@ -51,15 +51,19 @@ struct BwdArgs {
   const int32_t* cu_k;
   int B, Sq, Sk, H, Hkv, group;
   int num_units;
-  int num_k_blocks;  // per (unit, kv head)
+  int num_k_blocks;  // key blocks per (unit, kv head), dK/dV kernel
+  int num_q_blocks;  // query blocks per (unit, head), dQ kernel
   int lse_row;
   int rows_q;        // rows of q per head in total: B*Sq (dense) or total_q (packed)
   int rows_k;
+  int rotate;        // query-tile order: 0 = in order, 1 = spread by key block, 2 = offset kbi % 8
   float scale;
   float scale_log2;
 };
 
-enum class KernelId : int { Fwd = 0, FwdTail, Delta, Bwd, DqReduce, KvTail, Zero, Count };
+enum class KernelId : int {
+  Fwd = 0, FwdTail, Delta, BwdDkDv, BwdDq, BwdFused, DqReduce, KvTail, QTail, Zero, Count
+};
 
 const char* kernel_name(KernelId id);
 
@@ -69,7 +73,10 @@ hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool causal, int mask_mode
 hipError_t launch_fwd_tail(const FwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_delta(const BwdArgs& a, int head_dim, bool varlen, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool causal, int mask_mode, bool varlen,
-                      hipStream_t s);
+                      bool fused_dq, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, bool causal, int mask_mode, bool varlen,
+                         hipStream_t s);
+hipError_t launch_q_tail(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_dq_reduce(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_kv_tail(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_zero16(void* p, int64_t bytes, hipStream_t s);  // bytes % 16 == 0
@@ -77,7 +84,10 @@ hipError_t launch_zero16(void* p, int64_t bytes, hipStream_t s);  // bytes % 16 
 // Tile shapes the host needs for grid sizing, and the tiling selectors.
 int fwd_block_m(int head_dim, int mask, bool varlen);
 void set_fwd_variant(int v);
+void set_bwd_variant(int v);
+int get_bwd_variant();
 int get_fwd_variant();
 int bwd_block_n(int head_dim);
+int bwd_dq_block_m(int head_dim);
 
 }  // namespace exattn

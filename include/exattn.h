@@ -142,7 +142,8 @@ exattn_status exattn_check(const exattn_problem* p);
 exattn_status exattn_fwd(const exattn_problem* p, const void* q, const void* k,
                          const void* v, void* out, float* lse, void* stream);
 
-/* Bytes of device workspace exattn_bwd needs for this problem (0 on invalid input). */
+/* Bytes of device workspace exattn_bwd needs for this problem under the backward variant
+ * selected at the time of the call (see exattn_set_variant; 0 on invalid input). */
 size_t exattn_bwd_workspace_size(const exattn_problem* p);
 
 /*
@@ -151,8 +152,12 @@ size_t exattn_bwd_workspace_size(const exattn_problem* p);
  * outputs, contiguous, every element written. workspace: device memory of at least
  * exattn_bwd_workspace_size(p) bytes, 256-byte aligned, owned by the caller; its contents
  * on entry do not matter and on exit are unspecified. Concurrent calls must not share a
- * workspace. dq accumulates fp32 partial products with atomics, so it may differ between
- * runs by re-association of fp32 sums; out, lse, dk and dv are bitwise reproducible.
+ * workspace. With the default backward variant every output (dq included) is bitwise
+ * reproducible: each dq row is summed over keys in a fixed order by one workgroup. The
+ * fused variant accumulates dq with fp32 atomics instead, so there dq may differ between
+ * runs by re-association of fp32 sums, within the bound that PFCCLab cudnn-frontend PR #9
+ * states in "How it was verified" (an fp32 atomic accumulation is not bitwise stable
+ * against itself: cudnn-frontend PR #429, "API and compatibility impact").
  */
 exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, const void* v,
                          const void* out, const void* dout, const float* lse, void* dq,
@@ -180,9 +185,14 @@ int exattn_timing_read(const char** names, double* total_ms, int* launches, int 
  * variant 0 (default) = 8 waves x 32 query rows per workgroup with the lazy rescale
  * (threshold 8 in log2 units), 1 = the same tiling with an eager rescale on every tile,
  * 2 = 4 waves x 64 rows (lazy), 3 = 4 waves x 32 rows (lazy); 2 and 3 apply to head_dim
- * 128 without a mask or cu_seqlens, other problems fall back to 0. Every variant computes
- * the same function up to fp32 rounding. Process-wide; not thread-safe against concurrent
- * calls. Returns EXATTN_ERR_SHAPE for an unknown kernel or variant.
+ * 128 without a mask or cu_seqlens, other problems fall back to 0. `kernel` 1 = backward:
+ * 0 (default) = a dK/dV kernel (one workgroup per block of keys) and a separate dQ kernel
+ * (one workgroup per block of query rows, recomputing P and dP), no atomics, bitwise
+ * reproducible; 1 = one fused kernel that adds dQ partial products into an fp32 workspace
+ * accumulator with atomics, followed by a conversion pass (needs a larger workspace).
+ * Every variant computes the same function up to fp32 rounding. Process-wide; not
+ * thread-safe against concurrent calls. Returns EXATTN_ERR_SHAPE for an unknown kernel or
+ * variant.
  */
 exattn_status exattn_set_variant(int kernel, int variant);
 

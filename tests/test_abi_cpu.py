@@ -91,7 +91,7 @@ def test_check_accepts_valid_problem(lib):
     assert lib.exattn_check(ctypes.byref(_problem(head_dim=64, q_stride=(100 * 256, 256, 64),
                                                   k_stride=(77 * 128, 128, 64),
                                                   v_stride=(77 * 128, 128, 64)))) == 0
-    assert lib.exattn_bwd_workspace_size(ctypes.byref(_problem())) >= 2 * 100 * 4 * 128 * 4
+    assert lib.exattn_bwd_workspace_size(ctypes.byref(_problem())) >= 2 * 2 * 100 * 4 * 4
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -165,4 +165,12 @@ def test_set_variant(lib):
     for v in (1, 2, 3, 0):
         assert lib.exattn_set_variant(0, v) == 0
     assert lib.exattn_set_variant(0, 4) == 4
+    p = _problem()
+    ws = {}
+    for v in (1, 0):
+        assert lib.exattn_set_variant(1, v) == 0
+        ws[v] = lib.exattn_bwd_workspace_size(ctypes.byref(p))
+    # the fused variant also needs the fp32 dQ accumulator [rows_q, H, D]
+    assert ws[1] >= ws[0] + 2 * 100 * 4 * 128 * 4
+    assert lib.exattn_set_variant(1, 2) == 4
     assert lib.exattn_set_variant(7, 0) == 4

@@ -1,0 +1,83 @@
+"""Every selectable tiling computes the same function: the forward variants (8 or 4 waves,
+32 or 64 rows per wave, lazy or eager rescale) and the fused backward (fp32 dQ atomics)
+against the float64 oracle, and the lazy rescale against the eager one on widened logit
+spreads (FlyDSL PR #1033 "[Bugfix][Kernel] Fix NaN from the lazy rescale on a wide score
+range", "Test plan": no NaN, and not worse than the eager path)."""
+
+import pytest
+import torch
+
+from exact_attention_40_amd import api, workloads
+from gpu_util import (compare, dq_reassociation_bound, dq_runs_agree, nonfinite, run_gpu,
+                      run_oracle, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture
+def variant():
+    """Selects variants for one test and restores the defaults afterwards."""
+    yield api.set_variant
+    api.set_variant(0, 0)
+    api.set_variant(1, 0)
+
+
+FWD_CASES = [
+    dict(name="dense_d128", make=lambda: workloads.dense(2, 777, 650, 4, 2, 128, seed=7001)),
+    dict(name="causal_d128", make=lambda: workloads.dense(1, 900, 900, 4, 4, 128, seed=7002,
+                                                          causal=True)),
+    dict(name="bool_mask", make=lambda: workloads.padded_tile(360, 64, mask_kind="bool",
+                                                              seed=7003)),
+    dict(name="d64", make=lambda: workloads.dense(1, 300, 333, 2, 1, 64, seed=7004)),
+    dict(name="varlen", make=lambda: workloads.varlen_gqa(seed=7005, nseq=3, lmin=100,
+                                                          lmax=700, H=4, Hkv=2)),
+]
+
+
+@pytest.mark.parametrize("fwd_v", [0, 1, 2, 3])
+@pytest.mark.parametrize("case", FWD_CASES, ids=[c["name"] for c in FWD_CASES])
+def test_forward_variants(variant, fwd_v, case):
+    p = case["make"]()
+    variant(0, fwd_v)
+    compare(run_gpu(p, backward=False), run_oracle(p, backward=False),
+            names=("out", "lse"), tag=f"fwd v{fwd_v} {case['name']}")
+
+
+BWD_CASES = FWD_CASES + [
+    dict(name="additive_mask", make=lambda: workloads.padded_tile(392, 392, mask_kind="additive",
+                                                                  seed=7006)),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[c["name"] for c in BWD_CASES])
+def test_fused_backward_variant(variant, case):
+    """The fused backward matches the oracle, and its dq agrees with the default
+    backward's within the fp32 re-association bound of its atomics (dense problems). Its
+    key blocks visit the query tiles in a rotated order, so dk and dv are summed in another
+    order than the default backward's and are compared with the oracle only."""
+    p = case["make"]()
+    ref = run_oracle(p)
+    base = run_gpu(p)
+    variant(1, 1)
+    fused = run_gpu(p)
+    compare(fused, ref, tag=f"bwd fused {case['name']}")
+    if not p.varlen:
+        assert dq_runs_agree(fused["dq"], base["dq"], dq_reassociation_bound(p))
+
+
+@pytest.mark.parametrize("s", [8, 32, 64])
+def test_lazy_rescale_not_worse_than_eager(variant, s):
+    """k scaled by s (FlyDSL PR #1033, "Repro"): both rescale policies are finite and the
+    lazy one's error against the oracle is no larger than the eager one's (up to 10% and
+    a small absolute slack for rounding noise)."""
+    p = workloads.wide_logit(s, B=1, S=1536, H=2, D=128)
+    ref = run_oracle(p, backward=False)
+    errs = {}
+    for v in (0, 1):   # 0 = lazy (default), 1 = eager
+        variant(0, v)
+        g = run_gpu(p, backward=False)
+        assert nonfinite(g["out"]) == 0 and nonfinite(g["lse"]) == 0
+        errs[v] = compare(g, ref, names=("out", "lse"), tag=f"s={s} fwd v{v}")
+    for n in ("out", "lse"):
+        say(f"  s={s} {n}: lazy {errs[0][n]:.3e} eager {errs[1][n]:.3e}")
+        assert errs[0][n] <= 1.1 * errs[1][n] + 1e-4, n
