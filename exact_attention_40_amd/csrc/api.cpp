@@ -416,7 +416,7 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
 
 exattn_status exattn_set_variant(int kernel, int variant) {
   g_err[0] = 0;
-  if (kernel == 0 && variant >= 0 && variant <= 3) {
+  if (kernel == 0 && variant >= 0 && variant <= 2) {
     set_fwd_variant(variant);
     return EXATTN_OK;
   }

@@ -116,49 +116,6 @@ struct BwdTile {
   static_assert(DQ_TILES <= NW, "one dQ tile per wave at most");
 };
 
-// LDS model (64 banks of 4 bytes; 16-byte reads serve 16 lanes per cycle, 8-byte and
-// transposed reads 32 lanes per cycle). A row-major tile of 256-byte rows whose 16-byte
-// chunks are XOR-permuted by a 4x4 transpose of the row's low four bits,
-// chunk' = chunk ^ (4*(row & 3) + ((row >> 2) & 3)), is free of bank conflicts both for
-// 16-byte reads of 16 consecutive rows at one column and for transposed reads of 4
-// consecutive rows x 32 columns. Rows of D = 64 (128 bytes) keep the XOR inside 8 chunks.
-template <int D>
-__device__ __forceinline__ int swz_f(int row) {
-  const int f = 4 * (row & 3) + ((row >> 2) & 3);
-  return D == 128 ? f : (f & 7);
-}
-
-// Copy R rows of D bf16 (row stride `stride` elements, rows past the buffer range read as
-// zero) into a swizzled LDS tile with direct global->LDS loads: each wave instruction
-// fills 64 consecutive 16-byte LDS chunks, lane i the i-th, so lane i fetches the global
-// chunk that the swizzle places there. Completion is tracked by vmcnt.
-template <int D, int R, int NW>
-__device__ __forceinline__ void copy_tile_to_lds(unsigned char* dst, __amdgpu_buffer_rsrc_t rs,
-                                                 int stride, int wave, int lane) {
-  constexpr int CPR = D / 8;
-  constexpr int ITER = R * CPR / 64 / NW;
-#pragma unroll
-  for (int i = 0; i < ITER; ++i) {
-    const int p0 = (i * NW + wave) * 64;
-    const int pos = p0 + lane;
-    const int row = pos / CPR, pc = pos % CPR;
-    const int col = (pc ^ swz_f<D>(row)) * 8;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (__attribute__((address_space(3))) void*)(dst + p0 * 16), 16,
-        (int)((row * stride + col) * 2), 0, 0, 0);
-  }
-}
-
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Wait for every vector-memory operation except the most recent N. The counter retires in
-// issue order, so older loads are complete while the newest N (atomics) stay in flight.
-template <int N>
-__device__ __forceinline__ void wait_vmem_except() {
-  static_assert(N >= 0 && N <= 63, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 // LDS bytes: [K block | Q x2 | dO x2 | dS | P | lse2 x2 | Delta x2]; K block and dS only
 // when the kernel forms dQ.
 template <int D, bool DQ>
@@ -166,16 +123,6 @@ constexpr size_t bwd_smem_bytes() {
   using T = BwdTile<D>;
   return (size_t)((DQ ? T::K_ELEMS + T::S_ELEMS : 0) + 4 * T::Q_ELEMS) * 2 + T::P_BYTES +
          4 * T::BM * sizeof(float);
-}
-
-// LDS read at a per-lane byte address plus a compile-time byte offset (the offset folds into
-// the instruction's immediate field).
-template <class V>
-__device__ __forceinline__ V lds_at(const unsigned char* base, int imm) {
-  return *reinterpret_cast<const V*>(base + imm);
-}
-__device__ __forceinline__ bf16x4 tr_at(const unsigned char* base, int imm) {
-  return lds_read_tr4(reinterpret_cast<const bf16*>(base + imm));
 }
 
 template <int D, bool CAUSAL, int MASK, bool VARLEN, bool DQ>
@@ -307,11 +254,21 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
   const int rot = n_iter == 0 ? 0
                 : a.rotate == 1 ? (int)(((int64_t)kbi * n_iter) / a.num_k_blocks) % n_iter
                 : a.rotate == 2 ? (kbi & 7) % n_iter : 0;
-  auto tile_t = [&](int it) { int t = it + rot; return t >= n_iter ? t - n_iter : t; };
-  auto tile_head = [&](int it) { return g * a.group + tile_t(it) / n_qt; };
-  auto tile_q0 = [&](int it) { return qstart + (tile_t(it) % n_qt) * T::BM; };
-  auto load_q = [&](int it, int buf) {
-    const int head = tile_head(it), qt0 = tile_q0(it);
+  // Tile positions advance incrementally (query tile fastest, then head, wrapping), so the
+  // loop needs no integer division.
+  struct TilePos { int head, q0; };
+  const int h_beg = g * a.group, h_end = h_beg + a.group;
+  const int q_end = qstart + n_qt * T::BM;
+  auto advance = [&](TilePos& p) {
+    p.q0 += T::BM;
+    if (p.q0 >= q_end) {
+      p.q0 = qstart;
+      if (++p.head == h_end) p.head = h_beg;
+    }
+  };
+  TilePos cur = {h_beg + (n_iter ? rot / n_qt : 0), qstart + (n_iter ? rot % n_qt : 0) * T::BM};
+  auto load_q = [&](const TilePos& tp, int buf) {
+    const int head = tp.head, qt0 = tp.q0;
     const int rows = min(T::BM, Sq - qt0);
     const bf16* Qp = reinterpret_cast<const bf16*>(a.q) + qb_off + (int64_t)head * a.q_sh +
                      (int64_t)qt0 * a.q_ss;
@@ -339,22 +296,27 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
   // Prefetch distance two: tiles 0 and 1 now; tile it + 2 is requested during the dQ phase
   // of tile it, before that phase's atomics, so waiting for it never waits for atomics.
   if (n_iter > 0) {
-    load_q(0, 0);
+    load_q(cur, 0);
     store_stats(0);
   }
   if (n_iter > 1) {
     wait_vmem();
-    load_q(1, 1);
+    TilePos nx = cur;
+    advance(nx);
+    load_q(nx, 1);
     store_stats(1);
   }
   wait_vmem();
   __syncthreads();
 
   // One query tile. BUF (0/1) selects the staging buffer at compile time.
+  TilePos ahead = cur;   // position of tile it + 2
+  advance(ahead);
+  advance(ahead);
   auto iteration = [&](int it, auto buf_tag) {
     constexpr int BUF = decltype(buf_tag)::value;
     constexpr int QO = BUF * QBYTES;
-    const int head = tile_head(it), qt0 = tile_q0(it);
+    const int head = cur.head, qt0 = cur.q0;
     const bool edge = (kb0 + T::BN > Sk) || (qt0 + T::BM > Sq) || (MASK != kMaskNone) ||
                       (CAUSAL && kb0 + T::BN - 1 > qt0);
     const int64_t m_base = (int64_t)unit * a.m_sb + (int64_t)head * a.m_sh;
@@ -459,7 +421,8 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
     __syncthreads();  // dS complete; next tile's staging visible; P consumed
 
     // ---- phase 3: request tile it + 2, then the dQ tile of this wave over 128 keys ----
-    if (it + 2 < n_iter) load_q(it + 2, BUF);
+    if (it + 2 < n_iter) load_q(ahead, BUF);
+    advance(ahead);
     if (DQ && wave < T::DQ_TILES) {
       const int qb = wave / T::DB, db = dq_db;
       const int qrows = min(T::BM, Sq - qt0);
@@ -480,6 +443,7 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
             dq[r], rdq, (int)((row * a.H * D + db * 32 + l32) * 4), 0, 0);
       }
     }
+    advance(cur);
   };
 
   int it = 0;

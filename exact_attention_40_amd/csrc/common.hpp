@@ -63,27 +63,6 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-// Transpose a 4-row x 8-column bf16 block held as four 16-byte rows into eight 8-byte
-// columns (column c = rows 0..3 at column c), written as 64 contiguous bytes to `dst`.
-// This builds the "key-interleaved" tile layout T[row/4][col][row%4] that lets one lane
-// read four consecutive rows of one column with a single 8-byte LDS read.
-__device__ __forceinline__ void store_4x8_transposed(bf16* dst, u32x4 r0, u32x4 r1, u32x4 r2,
-                                                     u32x4 r3) {
-  u32x4 o[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // column 2j: low halves; column 2j+1: high halves
-    uint32_t a0 = (r0[j] & 0xffffu) | (r1[j] << 16);
-    uint32_t a1 = (r2[j] & 0xffffu) | (r3[j] << 16);
-    uint32_t b0 = (r0[j] >> 16) | (r1[j] & 0xffff0000u);
-    uint32_t b1 = (r2[j] >> 16) | (r3[j] & 0xffff0000u);
-    o[j] = u32x4{a0, a1, b0, b1};
-  }
-  u32x4* d = reinterpret_cast<u32x4*>(dst);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) d[j] = o[j];
-}
-
 // Map a hardware block index to a logical one so that consecutive logical blocks run on
 // the same XCD: the dispatcher places block b on XCD b % 8, each XCD having its own L2.
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
@@ -93,5 +72,70 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 }
 
 __device__ __forceinline__ float wave_xor32(float v) { return __shfl_xor(v, 32, 64); }
+
+// max and sum of the values held by lanes l and l ^ 32, on both lanes, in one
+// v_permlane32_swap (which exchanges the upper half of one register with the lower half of
+// another): the two results hold the lower and the upper half on every lane.
+__device__ __forceinline__ float pair_max32(float v) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+}
+__device__ __forceinline__ float pair_min32(float v) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fminf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+}
+
+// LDS model (64 banks of 4 bytes; 16-byte reads serve 16 lanes per cycle, 8-byte and
+// transposed reads 32 lanes per cycle). A row-major tile of 256-byte rows whose 16-byte
+// chunks are XOR-permuted by a 4x4 transpose of the row's low four bits,
+// chunk' = chunk ^ (4*(row & 3) + ((row >> 2) & 3)), is free of bank conflicts both for
+// 16-byte reads of 16 consecutive rows at one column and for transposed reads of 4
+// consecutive rows x 32 columns. Rows of D = 64 (128 bytes) keep the XOR inside 8 chunks.
+template <int D>
+__device__ __forceinline__ int swz_f(int row) {
+  const int f = 4 * (row & 3) + ((row >> 2) & 3);
+  return D == 128 ? f : (f & 7);
+}
+
+// Copy R rows of D bf16 (row stride `stride` elements, rows past the buffer range read as
+// zero) into a swizzled LDS tile with direct global->LDS loads: each wave instruction
+// fills 64 consecutive 16-byte LDS chunks, lane i the i-th, so lane i fetches the global
+// chunk that the swizzle places there. Completion is tracked by vmcnt.
+template <int D, int R, int NW>
+__device__ __forceinline__ void copy_tile_to_lds(unsigned char* dst, __amdgpu_buffer_rsrc_t rs,
+                                                 int stride, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int ITER = R * CPR / 64 / NW;
+#pragma unroll
+  for (int i = 0; i < ITER; ++i) {
+    const int p0 = (i * NW + wave) * 64;
+    const int pos = p0 + lane;
+    const int row = pos / CPR, pc = pos % CPR;
+    const int col = (pc ^ swz_f<D>(row)) * 8;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(dst + p0 * 16), 16,
+        (int)((row * stride + col) * 2), 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wait for every vector-memory operation except the most recent N. The counter retires in
+// issue order, so older loads are complete while the newest N (atomics) stay in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem_except() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS read at a per-lane byte address plus a compile-time byte offset (the offset folds into
+// the instruction's immediate field).
+template <class V>
+__device__ __forceinline__ V lds_at(const unsigned char* base, int imm) {
+  return *reinterpret_cast<const V*>(base + imm);
+}
+__device__ __forceinline__ bf16x4 tr_at(const unsigned char* base, int imm) {
+  return lds_read_tr4(reinterpret_cast<const bf16*>(base + imm));
+}
 
 }  // namespace exattn

@@ -8,22 +8,29 @@
 // removed inside the kernel (OpenWAM PR #64, "Summary"/"Fix").
 //
 // Work decomposition (gfx950, 64-wide waves):
-//   one workgroup = NW waves = one (unit, head, query tile of 32*QB*NW rows);
-//   each wave owns 32*QB query rows and keeps their Q fragments in registers;
-//   K and V tiles of 64 keys are staged through LDS, double-buffered through registers,
-//   loaded with buffer loads that return zero past the last key (no per-row branches).
+//   one workgroup = NW waves = one (unit, head, query tile of 32*NW rows); each wave owns
+//   32 query rows and keeps their Q fragments in registers; K and V tiles of 64 keys are
+//   copied straight from global memory into XOR-swizzled LDS (buffer loads with an LDS
+//   destination, zero past the last key), K one tile further ahead than V.
 // S^T = K Q^T is computed with 32x32x16 bf16 MFMAs so that a lane's accumulator holds one
 // query column: row statistics are per lane plus one exchange with the partner lane
 // (l ^ 32), the output rescale is a per-lane scalar, and the exponentiated scores feed
 // the O^T += V^T P^T MFMA as its B operand straight from registers. V stays row-major in
 // LDS; its A-operand fragments (four consecutive keys of one d per lane) come from
-// transposed LDS reads.
+// transposed LDS reads. The swizzle keeps both the K row reads and the V transposed reads
+// free of bank conflicts.
 //
-// Rescaling: EAGER takes m_new = max(m_row, m_tile) on every tile. The lazy form keeps the
-// running max while every row's tile max exceeds it by at most kLazyTau (log2 units), so
-// exponentials are bounded by 2^kLazyTau and the accumulator is left alone; as soon as one
-// row exceeds it, every lane takes max(m_row, m_tile) before exp2 (the FlyDSL PR #1033
-// fix: a lane dragged into the rescale by the wave-wide decision gets a factor <= 1).
+// Software pipeline: iteration t issues the S MFMAs of tile t+1 next to the exponentials of
+// tile t (independent work for the matrix and vector units of the same SIMD), then
+// O += V_t P_t next to the row max of tile t+1. The rescale for tile t+1 is decided after
+// that, outside the matrix work, so no branch splits the interleaved region.
+//
+// Rescaling: EAGER takes m_new = max(m_row, m_tile) whenever a row's max grows. The lazy
+// form keeps the running max while every row's tile max exceeds it by at most kLazyTau
+// (log2 units), so exponentials are bounded by 2^kLazyTau and the accumulator is left
+// alone; as soon as one row exceeds it, every lane takes max(m_row, m_tile) before exp2
+// (the FlyDSL PR #1033 fix: a lane dragged into the rescale by the wave-wide decision gets
+// a factor <= 1).
 
 #include <type_traits>
 
@@ -42,22 +49,25 @@ struct FwdTile {
   static constexpr int KB = BN / 32;
   static constexpr int DS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int KLD = D + 8;          // K row pitch: 16 B mod 128 B, conflict-free b128
-  static constexpr int VLD = D + 16;         // V row pitch: 32 B mod 128 B, conflict-free tr reads
-  static constexpr int K_ELEMS = BN * KLD;
-  static constexpr int V_ELEMS = BN * VLD;
-  static constexpr int CH = BN * D / 8 / NT; // 16-byte chunks per thread, per tensor
-  static_assert(CH * NT * 8 == BN * D, "tiles must split evenly over the threads");
+  static constexpr int RB = D * 2;           // bytes per LDS row (swizzled, no padding)
+  static constexpr int TBYTES = BN * RB;     // one K or V tile
+  static_assert((BN * D / 8) % NT == 0, "tiles must split evenly over the threads");
 };
 
 template <bool B>
 using bool_c = std::integral_constant<bool, B>;
+template <int I>
+using int_c = std::integral_constant<int, I>;
 
+// QB = 1: two waves per SIMD (8 waves x 32 rows); QB = 2: one wave per SIMD (4 waves x 64
+// rows), which halves the LDS reads per MFMA and relies on the in-stream interleave alone.
 template <int D, int NW, int QB, bool CAUSAL, int MASK, bool VARLEN, bool LAZY>
-__global__ void __launch_bounds__(64 * NW) fwd_kernel(FwdArgs a) {
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(QB == 1 ? 2 : 1)))
+fwd_kernel(FwdArgs a) {
   using T = FwdTile<D, NW, QB>;
-  __shared__ __attribute__((aligned(16))) bf16 k_lds[2 * T::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 v_lds[2 * T::V_ELEMS];
+  constexpr int RB = T::RB;
+  constexpr int V_OFF = 2 * T::TBYTES;           // V buffers follow the two K buffers
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * T::TBYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform across the wave
@@ -97,16 +107,23 @@ __global__ void __launch_bounds__(64 * NW) fwd_kernel(FwdArgs a) {
   const bf16* K = reinterpret_cast<const bf16*>(a.k) + k_base;
   const bf16* V = reinterpret_cast<const bf16*>(a.v) + v_base;
 
-  // Q fragments of this wave's rows, B-operand layout (column = query, k-slots = d).
-  const int qw0 = qt0 + wave * 32 * QB;
+  // A negative scale is folded into the sign of Q: (-q).k * |c| equals q.k * c exactly
+  // (negation commutes with every rounding), so the row max is always a max.
+  const float c2s = a.scale_log2;
+  const float c2 = fabsf(c2s);
+  const uint32_t qsign = c2s < 0.f ? 0x80008000u : 0u;
+
+  // Q fragments of this lane's query rows, B-operand layout (column = query, k-slots = d).
+  int qi[QB];
   bf16x8 qf[QB][T::DS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int qi = qw0 + qb * 32 + l32;
-    if (qi < Sq) {
-      const bf16* row = Q + (int64_t)qi * a.q_ss + 8 * half;
+    qi[qb] = qt0 + (wave * QB + qb) * 32 + l32;
+    if (qi[qb] < Sq) {
+      const bf16* row = Q + (int64_t)qi[qb] * a.q_ss + 8 * half;
 #pragma unroll
-      for (int s = 0; s < T::DS; ++s) qf[qb][s] = *reinterpret_cast<const bf16x8*>(row + 16 * s);
+      for (int s = 0; s < T::DS; ++s)
+        qf[qb][s] = __builtin_bit_cast(bf16x8, ldg16(row + 16 * s) ^ u32x4{qsign, qsign, qsign, qsign});
     } else {
 #pragma unroll
       for (int s = 0; s < T::DS; ++s) qf[qb][s] = bf16x8{};
@@ -123,232 +140,332 @@ __global__ void __launch_bounds__(64 * NW) fwd_kernel(FwdArgs a) {
     n_plain = min(lim, ntiles);
   }
 
-  // Per-thread 16-byte chunks of a tile: row and column are fixed, the tile base moves.
-  uint32_t k_off[T::CH], v_off[T::CH];
-  int lds_k[T::CH], lds_v[T::CH];
-#pragma unroll
-  for (int i = 0; i < T::CH; ++i) {
-    const int c = tid + i * T::NT;
-    const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-    k_off[i] = (uint32_t)(row * a.k_ss + col) * 2u;
-    v_off[i] = (uint32_t)(row * a.v_ss + col) * 2u;
-    lds_k[i] = row * T::KLD + col;
-    lds_v[i] = row * T::VLD + col;
-  }
-  u32x4 kr[T::CH], vr[T::CH];
-  auto load_tile = [&](int t) {
+  auto load_k = [&](int t, int buf) {
     const int kb0 = t * T::BN;
     const int rows = min(T::BN, Sk - kb0);
-    const auto rk = make_rsrc(K + (int64_t)kb0 * a.k_ss, (uint32_t)((rows - 1) * a.k_ss + D) * 2u);
-    const auto rv = make_rsrc(V + (int64_t)kb0 * a.v_ss, (uint32_t)((rows - 1) * a.v_ss + D) * 2u);
-#pragma unroll
-    for (int i = 0; i < T::CH; ++i) {
-      kr[i] = buf_load16(rk, k_off[i]);
-      vr[i] = buf_load16(rv, v_off[i]);
-    }
+    copy_tile_to_lds<D, T::BN, NW>(smem + buf * T::TBYTES,
+                                   make_rsrc(K + (int64_t)kb0 * a.k_ss, (uint32_t)((rows - 1) * a.k_ss + D) * 2u),
+                                   (int)a.k_ss, wave, lane);
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < T::CH; ++i) {
-      *reinterpret_cast<u32x4*>(k_lds + buf * T::K_ELEMS + lds_k[i]) = kr[i];
-      *reinterpret_cast<u32x4*>(v_lds + buf * T::V_ELEMS + lds_v[i]) = vr[i];
-    }
+  auto load_v = [&](int t, int buf) {
+    const int kb0 = t * T::BN;
+    const int rows = min(T::BN, Sk - kb0);
+    copy_tile_to_lds<D, T::BN, NW>(smem + V_OFF + buf * T::TBYTES,
+                                   make_rsrc(V + (int64_t)kb0 * a.v_ss, (uint32_t)((rows - 1) * a.v_ss + D) * 2u),
+                                   (int)a.v_ss, wave, lane);
   };
-  // Transposed-read address of this lane inside a V tile (16-lane group layout).
+  // Per-lane LDS bases. K row reads: key kb*32 + l32, 16-byte chunk 2*ds + half. V^T
+  // transposed reads: keys 16kk + 4*half + (j16>>2) + 8*sec, d = db*32 + 16*(grp&1) +
+  // 4*(j16&3). The swizzle depends on the row's low four bits only, so kb, kk and the
+  // buffer are immediate offsets.
   const int grp = lane >> 4, j16 = lane & 15;
-  const int v_rd = (4 * half + (j16 >> 2)) * T::VLD + 16 * (grp & 1) + 4 * (j16 & 3);
-
-  f32x16 o[T::DB][QB];
-  float m_run[QB], l_run[QB];
+  const unsigned char* ar[T::DS];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
+  for (int ds = 0; ds < T::DS; ++ds) ar[ds] = smem + l32 * RB + 16 * ((2 * ds + half) ^ swz_f<D>(l32));
+  const int clow = 2 * (grp & 1) + ((j16 & 3) >> 1);
+  const unsigned char* tv[T::DB][2];
 #pragma unroll
-    for (int db = 0; db < T::DB; ++db) o[db][qb] = f32x16{};
+  for (int sec = 0; sec < 2; ++sec) {
+    const int row = 4 * half + (j16 >> 2) + 8 * sec;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+      tv[db][sec] = smem + V_OFF + row * RB + 16 * ((4 * db + clow) ^ swz_f<D>(row)) + 8 * (j16 & 1);
   }
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  const float c2 = a.scale_log2;
   const uint8_t* mask_u8 = reinterpret_cast<const uint8_t*>(a.mask);
   const bf16* mask_bf = reinterpret_cast<const bf16*>(a.mask);
 
-  // Visibility of key kj for this lane's query in block qb, and its additive bias (log2).
-  auto visible = [&](int qb, int kj, float& b2) -> bool {
-    const int qi = qw0 + qb * 32 + l32;
-    bool vis = kj < Sk;
-    if (CAUSAL) vis = vis && (kj <= qi);
+  // Visibility of key kj for query row `row` and its additive bias in log2 units.
+  // Branch-free: the mask is read at indices clamped into [0, Sq) x [0, Sk), so every read
+  // is in range, and the result is used only for in-range pairs.
+  auto visible = [&](int row, int kj, float& b2) -> bool {
+    bool vis = (kj < Sk) && (row < Sq);
+    if (CAUSAL) vis = vis && (kj <= row);
     b2 = 0.f;
-    if (MASK == kMaskBool) {
-      if (vis && qi < Sq) vis = mask_u8[m_base + (int64_t)qi * a.m_si + kj] != 0;
-    }
-    if (MASK == kMaskAdd) {
-      if (vis && qi < Sq) {
-        const float bias = (float)mask_bf[m_base + (int64_t)qi * a.m_si + kj];
-        vis = bias != -INFINITY;
+    if (MASK != kMaskNone) {
+      const int64_t mi = m_base + (int64_t)min(row, Sq - 1) * a.m_si + min(kj, Sk - 1);
+      if (MASK == kMaskBool) {
+        vis = vis && (mask_u8[mi] != 0);
+      } else {
+        const float bias = (float)mask_bf[mi];
+        vis = vis && (bias != -INFINITY);
         b2 = vis ? bias * kLog2e : 0.f;
       }
     }
     return vis;
   };
 
-  auto tile = [&](int t, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const bf16* kl = k_lds + buf * T::K_ELEMS;
-    const bf16* vl = v_lds + buf * T::V_ELEMS;
+  f32x16 o[QB][T::DB];
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) o[qb][db] = f32x16{};
+  }
 
-    // S^T tile: rows = keys, columns = this wave's queries.
-    f32x16 s[T::KB][QB];
+  // Rescale decision for query block qb whose tile max is mt, wave-uniform. Eager:
+  // whenever some row's max grows (a factor of exactly 1 elsewhere leaves those rows
+  // unchanged). Lazy: only when some row's tile max exceeds its running max by more than
+  // kLazyTau. Per-row max first, then exp2: the factor is <= 1 on every lane.
+  auto update_max = [&](int qb, float mt) {
+    const float thr = LAZY ? kLazyTau : 0.f;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + thr) != 0) {
+      const float m_new = fmaxf(m_run[qb], mt);
+      const float corr = fast_exp2(m_run[qb] - ((m_new == -INFINITY) ? 0.f : m_new));
+      l_run[qb] *= corr;
 #pragma unroll
-    for (int kb = 0; kb < T::KB; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
-#pragma unroll
-    for (int ds = 0; ds < T::DS; ++ds) {
-#pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) {
-        const bf16x8 af =
-            *reinterpret_cast<const bf16x8*>(kl + (kb * 32 + l32) * T::KLD + ds * 16 + 8 * half);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma32(af, qf[qb][ds], s[kb][qb]);
-      }
+      for (int db = 0; db < T::DB; ++db) o[qb][db] *= corr;
+      m_run[qb] = m_new;
     }
+  };
 
-    const int kb0 = t * T::BN;
+  // Scores of tile t (cur) and t+1 (nxt): [QB][KB] accumulators, rows = keys, columns =
+  // this wave's queries. Element e of a score set is (qb, kb, r) = (e / (16 KB),
+  // (e / 16) % KB, e % 16), the order of every sweep below.
+  using Scores = f32x16[QB][T::KB];
+  constexpr int NE = QB * T::KB * 16;           // score elements per lane
+
+  // Row max of tile t's scores in log2 units (prologue only).
+  auto first_max = [&](const Scores& sc, int t, auto masked_tag, float (&mt)[QB]) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      // Tile max of the scaled scores, mt (log2 units); masked entries become -inf.
-      float mt;
-      if constexpr (!MASKED) {
-        float mx;
-        if (c2 >= 0.f) {
-          mx = -INFINITY;
+      float mx = -INFINITY;
 #pragma unroll
-          for (int kb = 0; kb < T::KB; ++kb)
+      for (int kb = 0; kb < T::KB; ++kb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-          mx = fmaxf(mx, wave_xor32(mx));
-        } else {
-          mx = INFINITY;
-#pragma unroll
-          for (int kb = 0; kb < T::KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fminf(mx, s[kb][qb][r]);
-          mx = fminf(mx, wave_xor32(mx));
-        }
-        mt = mx * c2;
-      } else {
-        // Masked tile: a visible entry contributes fma(s, c2, bias2) with bias2 the
-        // additive mask in log2 units (0 otherwise), the same rounding as the plain path.
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < T::KB; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < 16; ++r) {
+          if constexpr (!MASKED) {
+            mx = fmaxf(mx, sc[qb][kb][r]);
+          } else {
             float b2;
-            const bool vis = visible(qb, kb0 + kb * 32 + acc_row(r, half), b2);
-            mx = fmaxf(mx, vis ? fmaf(s[kb][qb][r], c2, b2) : -INFINITY);
-          }
-        }
-        mt = fmaxf(mx, wave_xor32(mx));
-      }
-      // Rescale decision, wave-uniform. Eager: whenever some row's max grows (a factor of
-      // exactly 1 elsewhere leaves those rows unchanged). Lazy: only when some row's tile
-      // max exceeds its running max by more than kLazyTau.
-      const float thr = LAZY ? kLazyTau : 0.f;
-      if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + thr) != 0) {
-        // Per-row max first, then exp2: the factor is <= 1 on every lane.
-        const float m_new = fmaxf(m_run[qb], mt);
-        const float corr = fast_exp2(m_run[qb] - ((m_new == -INFINITY) ? 0.f : m_new));
-        l_run[qb] *= corr;
-#pragma unroll
-        for (int db = 0; db < T::DB; ++db) o[db][qb] *= corr;
-        m_run[qb] = m_new;
-      }
-      const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-      float rs = 0.f;
-      if constexpr (!MASKED) {
-        const float nm = -m_use;
-#pragma unroll
-        for (int kb = 0; kb < T::KB; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(fmaf(s[kb][qb][r], c2, nm));
-            s[kb][qb][r] = p;
-            rs += p;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < T::KB; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float b2;
-            const bool vis = visible(qb, kb0 + kb * 32 + acc_row(r, half), b2);
-            const float p = vis ? fast_exp2(fmaf(s[kb][qb][r], c2, b2 - m_use)) : 0.f;
-            s[kb][qb][r] = p;
-            rs += p;
+            const bool vis = visible(qi[qb], t * T::BN + kb * 32 + acc_row(r, half), b2);
+            mx = fmaxf(mx, vis ? fmaf(sc[qb][kb][r], c2, b2) : -INFINITY);
           }
         }
       }
-      l_run[qb] += rs;
+      mx = pair_max32(mx);
+      mt[qb] = MASKED ? mx : mx * c2;
     }
+  };
 
-    // O^T += V^T P^T over 16-key slabs; V^T fragments by transposed reads.
+  // Iteration body as one instruction stream:
+  //   QK phase: the S MFMAs of tile t+1 (16 K fragments, each used for QB MFMAs; fragments
+  //             read three ahead) with two exponentials of tile t per MFMA, and the
+  //             transposed V reads for the first two PV slabs over the last 8 fragments;
+  //   PV phase: the PV MFMAs of tile t (each V fragment used for QB MFMAs) with two
+  //             elements of tile t+1's row max per MFMA and the remaining V reads two slabs
+  //             ahead.
+  // Scheduling fences (only scalar instructions may cross) keep this order, so the matrix
+  // and vector work of one wave overlap. MC / MN: tile t / t+1 needs masking. Unmasked,
+  // the row max of s * c2 is c2 * max(s) (c2 >= 0); masked, a visible entry counts as
+  // fma(s, c2, bias2), the rounding the exponent uses. Writes tile t+1's row max (log2
+  // units) to mt.
+  auto body = [&](Scores& nxt, Scores& cur, int t, auto par_tag, auto mc_tag, auto mn_tag,
+                  float (&mt)[QB]) {
+    constexpr int PAR = decltype(par_tag)::value;
+    constexpr bool MC = decltype(mc_tag)::value;
+    constexpr bool MN = decltype(mn_tag)::value;
+    constexpr int KO = (PAR ^ 1) * T::TBYTES;   // K of tile t + 1
+    constexpr int VB = PAR * T::TBYTES;         // V of tile t
+    constexpr int NF = T::DS * T::KB;           // K fragments
+    constexpr int QSTEPS = NF * QB;             // S MFMAs
+    constexpr int NKK = T::BN / 16;             // PV slabs
+    constexpr int PSTEPS = NKK * T::DB * QB;    // PV MFMAs
+    constexpr int PER = NE / QSTEPS;            // exponentials per S MFMA
+    constexpr int MPER = NE / PSTEPS;           // max elements per PV MFMA
+    static_assert(NF >= 8 && NKK == 4 && PER * QSTEPS == NE && MPER * PSTEPS == NE &&
+                  MPER % 2 == 0 && (16 * T::KB) % MPER == 0, "schedule shape");
+    const int kc0 = t * T::BN, kn0 = kc0 + T::BN;
+    float m_use[QB], rs[QB][4];
 #pragma unroll
-    for (int kk = 0; kk < T::BN / 16; ++kk) {
+    for (int qb = 0; qb < QB; ++qb) {
+      m_use[qb] = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rs[qb][j] = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb) nxt[qb][kb] = f32x16{};
+    }
+    auto kfrag = [&](int f) { return lds_at<bf16x8>(ar[f / T::KB], KO + (f % T::KB) * 32 * RB); };
+    auto vfrag = [&](int kk, int db, int sec) { return tr_at(tv[db][sec], VB + 16 * kk * RB); };
+    bf16x8 kf[3] = {kfrag(0), kfrag(1), kfrag(2)};
+    bf16x4 vt[2][T::DB][2];
+#pragma unroll
+    for (int i = 0; i < QSTEPS; ++i) {
+      const int f = i / QB, qb = i % QB;
+      const int ds = f / T::KB, kb = f % T::KB;
+      nxt[qb][kb] = mfma32(kf[f % 3], qf[qb][ds], nxt[qb][kb]);
+      if (qb == QB - 1 && f + 3 < NF) kf[f % 3] = kfrag(f + 3);
+      // transposed reads of slabs 0 and 1 over the last eight fragments
+      const int j = f - (NF - 8);
+      if (qb == 0 && j >= 0) {
+        const int kk = j / 4, db = j % 4;
+        if (db < T::DB) {
+          vt[kk][db][0] = vfrag(kk, db, 0);
+          vt[kk][db][1] = vfrag(kk, db, 1);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int e = PER * i + u;
+        const int eq = e / (16 * T::KB), cb = (e / 16) % T::KB, r = e % 16;
+        float pe;
+        if constexpr (!MC) {
+          pe = fast_exp2(fmaf(cur[eq][cb][r], c2, -m_use[eq]));
+        } else {
+          float b2;
+          const bool vis = visible(qi[eq], kc0 + cb * 32 + acc_row(r, half), b2);
+          pe = vis ? fast_exp2(fmaf(cur[eq][cb][r], c2, b2 - m_use[eq])) : 0.f;
+        }
+        cur[eq][cb][r] = pe;
+        rs[eq][r & 3] += pe;
+        asm volatile("" : "+v"(rs[eq][r & 3]));   // pin this step's exponential and sum here
+      }
+      __builtin_amdgcn_sched_barrier(0x0004);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      asm volatile("" : "+v"(rs[qb][0]), "+v"(rs[qb][1]), "+v"(rs[qb][2]), "+v"(rs[qb][3]));
+      l_run[qb] += (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
+    }
+    float mx[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mx[qb] = -INFINITY;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
       const int kb = kk >> 1, hs = (kk & 1) * 8;
       bf16x8 pf[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-        pf[qb] = cvt8(s[kb][qb][hs + 0], s[kb][qb][hs + 1], s[kb][qb][hs + 2], s[kb][qb][hs + 3],
-                      s[kb][qb][hs + 4], s[kb][qb][hs + 5], s[kb][qb][hs + 6], s[kb][qb][hs + 7]);
+        pf[qb] = cvt8(cur[qb][kb][hs + 0], cur[qb][kb][hs + 1], cur[qb][kb][hs + 2],
+                      cur[qb][kb][hs + 3], cur[qb][kb][hs + 4], cur[qb][kb][hs + 5],
+                      cur[qb][kb][hs + 6], cur[qb][kb][hs + 7]);
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) {
-        // slots 0-3: keys 16kk + 4h + 0..3, slots 4-7: keys 16kk + 8 + 4h + 0..3
-        const bf16* vp = vl + (16 * kk) * T::VLD + db * 32 + v_rd;
-        const bf16x8 af = cat44(lds_read_tr4(vp), lds_read_tr4(vp + 8 * T::VLD));
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma32(af, pf[qb], o[db][qb]);
+        for (int qb = 0; qb < QB; ++qb) {
+          o[qb][db] = mfma32(cat44(vt[kk & 1][db][0], vt[kk & 1][db][1]), pf[qb], o[qb][db]);
+          if (qb == QB - 1 && kk + 2 < NKK) {
+            vt[kk & 1][db][0] = vfrag(kk + 2, db, 0);
+            vt[kk & 1][db][1] = vfrag(kk + 2, db, 1);
+          }
+          const int step = (kk * T::DB + db) * QB + qb;
+#pragma unroll
+          for (int u = 0; u < MPER; u += 2) {
+            // a pair never straddles two query blocks (16 KB is a multiple of MPER)
+            const int e0 = MPER * step + u, e1 = e0 + 1;
+            const int q0 = e0 / (16 * T::KB), b0i = (e0 / 16) % T::KB, r0 = e0 % 16;
+            const int b1i = (e1 / 16) % T::KB, r1 = e1 % 16;
+            float x0 = nxt[q0][b0i][r0], x1 = nxt[q0][b1i][r1];
+            if constexpr (MN) {
+              float bb0, bb1;
+              const bool v0 = visible(qi[q0], kn0 + b0i * 32 + acc_row(r0, half), bb0);
+              const bool v1 = visible(qi[q0], kn0 + b1i * 32 + acc_row(r1, half), bb1);
+              x0 = v0 ? fmaf(x0, c2, bb0) : -INFINITY;
+              x1 = v1 ? fmaf(x1, c2, bb1) : -INFINITY;
+            }
+            mx[q0] = fmaxf(fmaxf(mx[q0], x0), x1);
+            asm volatile("" : "+v"(mx[q0]));   // pin this step's part of the max chain here
+          }
+          __builtin_amdgcn_sched_barrier(0x0004);
+        }
       }
     }
-
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      asm volatile("" : "+v"(mx[qb]));   // keep the max chain inside the stream
+      mt[qb] = MN ? pair_max32(mx[qb]) : pair_max32(mx[qb]) * c2;
+    }
   };
 
+  // Tile j's K lives in K buffer j & 1 and its V in V buffer j & 1.
+  Scores sa, sb;
+  if (ntiles > 0) {
+    load_k(0, 0);
+    load_v(0, 0);
+  }
+  if (ntiles > 1) load_k(1, 1);
+  wait_vmem();
+  __syncthreads();
+  if (ntiles > 0) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb) sa[qb][kb] = f32x16{};
+    }
+#pragma unroll
+    for (int ds = 0; ds < T::DS; ++ds) {
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb) {
+        const bf16x8 kfr = lds_at<bf16x8>(ar[ds], kb * 32 * RB);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sa[qb][kb] = mfma32(kfr, qf[qb][ds], sa[qb][kb]);
+      }
+    }
+    float mt[QB];
+    if (n_plain > 0) first_max(sa, 0, bool_c<false>{}, mt);
+    else first_max(sa, 0, bool_c<true>{}, mt);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) update_max(qb, mt[qb]);
+  }
+  __syncthreads();  // every wave has read K_0 before K_2 replaces it
+
+  // Iteration t. Buffers: K tile t (parity PAR) was consumed by the previous iteration and
+  // is refilled with K_{t+2}; V buffer PAR ^ 1 (V_{t-1}) is refilled with V_{t+1}. When
+  // t + 1 == ntiles the S MFMAs read a stale K buffer and their result is discarded.
+  auto iteration = [&](int t, Scores& cur, Scores& nxt, auto par_tag, auto mask_cur,
+                       auto mask_nxt) {
+    constexpr int PAR = decltype(par_tag)::value;
+    if (t + 2 < ntiles) load_k(t + 2, PAR);
+    if (t + 1 < ntiles) load_v(t + 1, PAR ^ 1);
+    float mt[QB];
+    body(nxt, cur, t, par_tag, mask_cur, mask_nxt, mt);
+    if (t + 1 < ntiles) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) update_max(qb, mt[qb]);
+    }
+    wait_vmem();      // this wave's part of K_{t+2} and V_{t+1} has landed in LDS
+    __syncthreads();  // ... every wave's part; every wave is done with K_{t+1} and V_t
+  };
+
+  using F = bool_c<false>;
+  using Tr = bool_c<true>;
   int t = 0;
-  for (; t < n_plain; ++t) tile(t, bool_c<false>{});
-  for (; t < ntiles; ++t) tile(t, bool_c<true>{});
+  for (; t + 2 < n_plain; t += 2) {
+    iteration(t, sa, sb, int_c<0>{}, F{}, F{});
+    iteration(t + 1, sb, sa, int_c<1>{}, F{}, F{});
+  }
+  // Remaining tiles (the masked ones and at most two unmasked ones before them) take the
+  // masked form, still in pairs so that the pending scores of the next tile live in sa at
+  // the top of the loop. One form per loop keeps the register allocation of the two loops
+  // independent (a run-time choice between forms inside one loop costs spills).
+  for (; t < ntiles; t += 2) {
+    iteration(t, sa, sb, int_c<0>{}, Tr{}, Tr{});
+    if (t + 1 < ntiles) iteration(t + 1, sb, sa, int_c<1>{}, Tr{}, Tr{});
+  }
 
   // Epilogue: normalise, write out (bf16, RNE) and lse (natural log).
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int qi = qw0 + qb * 32 + l32;
     const float l = l_run[qb] + wave_xor32(l_run[qb]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    if (qi < Sq) {
-      bf16* orow = reinterpret_cast<bf16*>(a.out) + o_base + (int64_t)qi * a.o_ss;
+    if (qi[qb] < Sq) {
+      bf16* orow = reinterpret_cast<bf16*>(a.out) + o_base + (int64_t)qi[qb] * a.o_ss;
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) {
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const int d = db * 32 + 8 * rg + 4 * half;
-          f32x4 vv = {o[db][qb][4 * rg + 0] * inv, o[db][qb][4 * rg + 1] * inv,
-                      o[db][qb][4 * rg + 2] * inv, o[db][qb][4 * rg + 3] * inv};
+          f32x4 vv = {o[qb][db][4 * rg + 0] * inv, o[qb][db][4 * rg + 1] * inv,
+                      o[qb][db][4 * rg + 2] * inv, o[qb][db][4 * rg + 3] * inv};
           *reinterpret_cast<bf16x4*>(orow + d) = __builtin_convertvector(vv, bf16x4);
         }
       }
       if (half == 0) {
         const float mu = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-        a.lse[lse_base + qi] = l > 0.f ? (mu + log2f(l)) * kLn2 : -INFINITY;
+        a.lse[lse_base + qi[qb]] = l > 0.f ? (mu + log2f(l)) * kLn2 : -INFINITY;
       }
     }
   }
@@ -368,22 +485,21 @@ __global__ void __launch_bounds__(256) fwd_tail_kernel(FwdArgs a) {
 }
 
 // Variants: 0 = 8 waves x 32 rows, lazy rescale (default); 1 = 8 waves x 32 rows, eager
-// rescale; 2 = 4 waves x 64 rows, lazy; 3 = 4 waves x 32 rows, lazy. Variants 2 and 3 are
-// compiled for head_dim 128 without a mask; other problems use variant 0 or 1.
+// rescale; 2 = 4 waves x 64 rows (lazy), one wave per SIMD. Variant 2 is compiled for
+// head_dim 128 without a mask or cu_seqlens; other problems use variant 0.
 static int g_fwd_variant = 0;
 
-void set_fwd_variant(int v) { g_fwd_variant = (v >= 0 && v <= 3) ? v : 0; }
+void set_fwd_variant(int v) { g_fwd_variant = (v >= 0 && v <= 2) ? v : 0; }
 int get_fwd_variant() { return g_fwd_variant; }
 
 static int effective_variant(int head_dim, int mask, bool varlen) {
   const int v = g_fwd_variant;
-  if (v >= 2 && (head_dim != 128 || mask != kMaskNone || varlen)) return 0;
+  if (v == 2 && (head_dim != 128 || mask != kMaskNone || varlen)) return 0;
   return v;
 }
 
 int fwd_block_m(int head_dim, int mask, bool varlen) {
-  const int v = effective_variant(head_dim, mask, varlen);
-  return v == 2 ? 256 : (v == 3 ? 128 : 256);
+  return 256;
 }
 
 template <int D, int NW, int QB, bool LAZY>
@@ -430,7 +546,6 @@ hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool causal, int mask, boo
   }
   if (v == 1) return launch_fwd_d<128, 8, 1, false>(a, causal, mask, varlen, s);
   if (v == 2) return launch_fwd_plain128<4, 2>(a, causal, s);
-  if (v == 3) return launch_fwd_plain128<4, 1>(a, causal, s);
   return launch_fwd_d<128, 8, 1, true>(a, causal, mask, varlen, s);
 }
 

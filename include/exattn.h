@@ -183,9 +183,10 @@ int exattn_timing_read(const char** names, double* total_ms, int* launches, int 
 /*
  * Tiling selection, for benchmarking the compiled alternatives. `kernel` 0 = forward:
  * variant 0 (default) = 8 waves x 32 query rows per workgroup with the lazy rescale
- * (threshold 8 in log2 units), 1 = the same tiling with an eager rescale on every tile,
- * 2 = 4 waves x 64 rows (lazy), 3 = 4 waves x 32 rows (lazy); 2 and 3 apply to head_dim
- * 128 without a mask or cu_seqlens, other problems fall back to 0. `kernel` 1 = backward:
+ * (threshold 8 in log2 units), 1 = the same tiling with an eager rescale whenever a row
+ * max grows, 2 = 4 waves x 32 rows (lazy), two workgroups per compute unit; 2 applies to
+ * head_dim 128 without a mask or cu_seqlens, other problems fall back to 0. `kernel` 1 =
+ * backward:
  * 0 (default) = a dK/dV kernel (one workgroup per block of keys) and a separate dQ kernel
  * (one workgroup per block of query rows, recomputing P and dP), no atomics, bitwise
  * reproducible; 1 = one fused kernel that adds dQ partial products into an fp32 workspace

@@ -162,9 +162,9 @@ def test_timing_read_empty(lib):
 
 
 def test_set_variant(lib):
-    for v in (1, 2, 3, 0):
+    for v in (1, 2, 0):
         assert lib.exattn_set_variant(0, v) == 0
-    assert lib.exattn_set_variant(0, 4) == 4
+    assert lib.exattn_set_variant(0, 3) == 4
     p = _problem()
     ws = {}
     for v in (1, 0):

@@ -1,5 +1,5 @@
-"""Every selectable tiling computes the same function: the forward variants (8 or 4 waves,
-32 or 64 rows per wave, lazy or eager rescale) and the fused backward (fp32 dQ atomics)
+"""Every selectable tiling computes the same function: the forward variants (8 or 4 waves
+per workgroup, lazy or eager rescale) and the fused backward (fp32 dQ atomics)
 against the float64 oracle, and the lazy rescale against the eager one on widened logit
 spreads (FlyDSL PR #1033 "[Bugfix][Kernel] Fix NaN from the lazy rescale on a wide score
 range", "Test plan": no NaN, and not worse than the eager path)."""
@@ -34,7 +34,7 @@ FWD_CASES = [
 ]
 
 
-@pytest.mark.parametrize("fwd_v", [0, 1, 2, 3])
+@pytest.mark.parametrize("fwd_v", [0, 1, 2])
 @pytest.mark.parametrize("case", FWD_CASES, ids=[c["name"] for c in FWD_CASES])
 def test_forward_variants(variant, fwd_v, case):
     p = case["make"]()
