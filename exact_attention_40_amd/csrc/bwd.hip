@@ -689,21 +689,11 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
     }
   }
 
-  // Epilogue: dq = bf16(dQ * scale), dense [rows_q, H, D]; rows past Sq are not written.
-  if (qi < Sq) {
-    bf16* row = reinterpret_cast<bf16*>(a.dq) + ((qrow0 + qi) * a.H + head) * D;
-    const float sc = a.scale;
-#pragma unroll
-    for (int db = 0; db < T::DB; ++db) {
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d = db * 32 + 8 * rg + 4 * half;
-        f32x4 vv = {dq[db][4 * rg] * sc, dq[db][4 * rg + 1] * sc, dq[db][4 * rg + 2] * sc,
-                    dq[db][4 * rg + 3] * sc};
-        *reinterpret_cast<bf16x4*>(row + d) = __builtin_convertvector(vv, bf16x4);
-      }
-    }
-  }
+  // Epilogue: dq = bf16(dQ * scale), contiguous [rows_q, H, D], through this wave's slice
+  // of LDS (free after the last barrier); rows past Sq are not written.
+  bf16* dqw = reinterpret_cast<bf16*>(a.dq) + ((qrow0 + qw0) * a.H + head) * D;
+  static_assert(T::NW * 32 * D * 2 <= 4 * T::TBYTES, "epilogue staging fits the tile buffers");
+  wave_store_rows<D>(smem + wave * 32 * D * 2, dq, a.scale, dqw, (int64_t)a.H * D, Sq - qw0, lane);
 }
 
 // ----------------------------------------------------------------------------------------

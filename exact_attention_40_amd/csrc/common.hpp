@@ -138,4 +138,41 @@ __device__ __forceinline__ bf16x4 tr_at(const unsigned char* base, int imm) {
   return lds_read_tr4(reinterpret_cast<const bf16*>(base + imm));
 }
 
+// Store a wave's 32 x D result block as bf16 rows, coalesced. `acc[db]` holds the block in
+// the MFMA result layout with lane = row (l % 32) and register r = column db*32 +
+// acc_row(r, l / 32). The values go through this wave's own 32 * D * 2 bytes of LDS `buf`
+// (16-byte chunks XOR-swizzled by the row's low bits, so both the 8-byte writes and the
+// 16-byte reads avoid bank conflicts), then each lane stores 16 contiguous bytes: every
+// store instruction covers whole rows. Rows r >= nrows are not written. The caller makes
+// sure no other wave uses `buf` meanwhile.
+template <int D>
+__device__ __forceinline__ void wave_store_rows(unsigned char* buf, const f32x16 (&acc)[D / 32],
+                                                float scale, bf16* dst, int64_t row_stride,
+                                                int nrows, int lane) {
+  constexpr int RB = D * 2;
+  constexpr int CPR = D / 8;                     // 16-byte chunks per row
+  const int half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int c8 = db * 8 + 2 * rg + half;     // 8-byte chunk of columns 4*c8 .. 4*c8+3
+      f32x4 v = {acc[db][4 * rg] * scale, acc[db][4 * rg + 1] * scale, acc[db][4 * rg + 2] * scale,
+                 acc[db][4 * rg + 3] * scale};
+      *reinterpret_cast<bf16x4*>(buf + l32 * RB + 16 * ((c8 >> 1) ^ (l32 & (CPR - 1))) + 8 * (c8 & 1)) =
+          __builtin_convertvector(v, bf16x4);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int RPI = 64 / CPR;                  // rows per instruction
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CPR, c = lane % CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(buf + r * RB + 16 * (c ^ (r & (CPR - 1))));
+    if (r < nrows) *reinterpret_cast<u32x4*>(dst + (int64_t)r * row_stride + 8 * c) = v;
+  }
+}
+
 }  // namespace exattn

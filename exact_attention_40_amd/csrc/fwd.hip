@@ -446,27 +446,20 @@ fwd_kernel(FwdArgs a) {
     if (t + 1 < ntiles) iteration(t + 1, sb, sa, int_c<1>{}, Tr{}, Tr{});
   }
 
-  // Epilogue: normalise, write out (bf16, RNE) and lse (natural log).
+  // Epilogue: normalise, write out (bf16, RNE) through this wave's slice of LDS (every wave
+  // has passed the last barrier, so the K/V buffers are free) and lse (natural log).
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l = l_run[qb] + wave_xor32(l_run[qb]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    if (qi[qb] < Sq) {
-      bf16* orow = reinterpret_cast<bf16*>(a.out) + o_base + (int64_t)qi[qb] * a.o_ss;
-#pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int d = db * 32 + 8 * rg + 4 * half;
-          f32x4 vv = {o[qb][db][4 * rg + 0] * inv, o[qb][db][4 * rg + 1] * inv,
-                      o[qb][db][4 * rg + 2] * inv, o[qb][db][4 * rg + 3] * inv};
-          *reinterpret_cast<bf16x4*>(orow + d) = __builtin_convertvector(vv, bf16x4);
-        }
-      }
-      if (half == 0) {
-        const float mu = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-        a.lse[lse_base + qi[qb]] = l > 0.f ? (mu + log2f(l)) * kLn2 : -INFINITY;
-      }
+    const int r0 = qt0 + (wave * QB + qb) * 32;
+    bf16* orow = reinterpret_cast<bf16*>(a.out) + o_base + (int64_t)r0 * a.o_ss;
+    static_assert(NW * QB * 32 * D * 2 <= 4 * T::TBYTES, "epilogue staging fits the tile buffers");
+    wave_store_rows<D>(smem + (wave * QB + qb) * 32 * D * 2, o[qb], inv, orow, a.o_ss,
+                       Sq - r0, lane);
+    if (qi[qb] < Sq && half == 0) {
+      const float mu = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+      a.lse[lse_base + qi[qb]] = l > 0.f ? (mu + log2f(l)) * kLn2 : -INFINITY;
     }
   }
 }
