@@ -37,6 +37,9 @@ def _norm(t: torch.Tensor) -> torch.Tensor:
     return t if ok else t.contiguous()
 
 
+_DTYPES = {torch.bfloat16: _lib.DTYPE_BF16, torch.float16: _lib.DTYPE_FP16}
+
+
 def _strides3(t: torch.Tensor, varlen: bool):
     if varlen:  # [T, H, D]
         return (0, t.stride(0), t.stride(1))
@@ -55,8 +58,12 @@ class _Spec:
                 raise ValueError(f"{name} must be on a GPU device, got {t.device}")
             if t.device != q.device:
                 raise ValueError(f"{name} is on {t.device}, q is on {q.device}")
-            if t.dtype != torch.bfloat16:
-                raise ValueError(f"{name} has dtype {t.dtype}; only torch.bfloat16 is supported")
+            if t.dtype not in _DTYPES:
+                raise ValueError(f"{name} has dtype {t.dtype}; torch.bfloat16 or torch.float16 "
+                                 "is supported")
+            if t.dtype != q.dtype:
+                raise ValueError(f"{name} has dtype {t.dtype}, q has {q.dtype}")
+        self.dtype = q.dtype
         self.varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
         if self.varlen:
             if cu_seqlens_q is None or cu_seqlens_k is None:
@@ -165,7 +172,7 @@ class _Spec:
     def problem(self, q, k, v, side, out=None, dout=None):
         mask_kind, mask_t, mask_stride, cu_q, cu_k, nseq, max_q, max_k = side
         p = _lib.Problem()
-        p.dtype = _lib.DTYPE_BF16
+        p.dtype = _DTYPES[self.dtype]
         p.batch = self.batch
         p.seqlen_q, p.seqlen_k = self.sq, self.sk
         p.heads_q, p.heads_kv, p.head_dim = self.H, self.Hkv, self.D
@@ -215,7 +222,8 @@ def exattn_fwd(q, k, v, *, causal=False, scale=None, mask=None, cu_seqlens_q=Non
 
     Dense: q [B, Sq, H, D], k/v [B, Sk, Hkv, D] -> out [B, Sq, H, D], lse [B, H, Sq] fp32.
     Packed: q [Tq, H, D], k/v [Tk, Hkv, D] with int32 cu_seqlens -> out [Tq, H, D],
-    lse [H, Tq]. mask: bool (True = attend) or additive bf16, broadcastable to
+    lse [H, Tq]. q, k, v are bf16 or fp16 (all the same); out has their dtype.
+    mask: bool (True = attend) or additive bf16 (for either input dtype), broadcastable to
     [B, H, Sq, Sk]. lse is the natural-log log-sum-exp; empty rows give out 0, lse -inf.
     """
     lib = _lib.load()
@@ -226,7 +234,7 @@ def exattn_fwd(q, k, v, *, causal=False, scale=None, mask=None, cu_seqlens_q=Non
         with torch.cuda.stream(stream):
             side = spec.prepare_side_inputs(q.device)
             qn, kn, vn = _norm(q), _norm(k), _norm(v)
-            out = torch.empty(spec.q_shape, dtype=torch.bfloat16, device=q.device)
+            out = torch.empty(spec.q_shape, dtype=spec.dtype, device=q.device)
             lse = torch.empty(spec.lse_shape, dtype=torch.float32, device=q.device)
             p = spec.problem(qn, kn, vn, side)
             st = lib.exattn_fwd(ctypes.byref(p), _ptr(qn), _ptr(kn), _ptr(vn), _ptr(out),
@@ -264,8 +272,8 @@ def exattn_bwd(q, k, v, out, dout, lse, *, causal=False, scale=None, mask=None,
                              f"{None if not isinstance(t, torch.Tensor) else tuple(t.shape)}")
         if t.device != q.device:
             raise ValueError(f"{name} is on {t.device}, q is on {q.device}")
-        if t.dtype != torch.bfloat16:
-            raise ValueError(f"{name} has dtype {t.dtype}; only torch.bfloat16 is supported")
+        if t.dtype != spec.dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}; q has {spec.dtype}")
     if not isinstance(lse, torch.Tensor) or tuple(lse.shape) != spec.lse_shape:
         raise ValueError(f"lse must have shape {spec.lse_shape}, got "
                          f"{None if not isinstance(lse, torch.Tensor) else tuple(lse.shape)}")
@@ -277,9 +285,9 @@ def exattn_bwd(q, k, v, out, dout, lse, *, causal=False, scale=None, mask=None,
             side = spec.prepare_side_inputs(q.device)
             qn, kn, vn, on, don = _norm(q), _norm(k), _norm(v), _norm(out), _norm(dout)
             lsen = lse.contiguous()
-            dq = torch.empty(spec.q_shape, dtype=torch.bfloat16, device=q.device)
-            dk = torch.empty(tuple(k.shape), dtype=torch.bfloat16, device=q.device)
-            dv = torch.empty(tuple(v.shape), dtype=torch.bfloat16, device=q.device)
+            dq = torch.empty(spec.q_shape, dtype=spec.dtype, device=q.device)
+            dk = torch.empty(tuple(k.shape), dtype=spec.dtype, device=q.device)
+            dv = torch.empty(tuple(v.shape), dtype=spec.dtype, device=q.device)
             p = spec.problem(qn, kn, vn, side, out=on, dout=don)
             ws_bytes = int(lib.exattn_bwd_workspace_size(ctypes.byref(p)))
             ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=q.device)
@@ -320,7 +328,7 @@ class AttnFunction(torch.autograd.Function):
 
 def attention(q, k, v, causal=False, scale=None, mask=None, cu_seqlens_q=None,
               cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None):
-    """Differentiable attention output (bf16)."""
+    """Differentiable attention output (in q's dtype, bf16 or fp16)."""
     return AttnFunction.apply(q, k, v, causal, scale, mask, cu_seqlens_q, cu_seqlens_k,
                               max_seqlen_q, max_seqlen_k)
 

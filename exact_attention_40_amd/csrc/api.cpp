@@ -106,8 +106,8 @@ exattn_status check_strides(const int64_t* st, bool varlen, const char* name) {
 
 exattn_status validate(const exattn_problem* p, bool bwd) {
   if (!p) return fail(EXATTN_ERR_NULL, "problem pointer is NULL");
-  if (p->dtype != EXATTN_DTYPE_BF16)
-    return fail(EXATTN_ERR_DTYPE, "dtype %d is not supported: only bf16 (0) is accepted", p->dtype);
+  if (p->dtype != EXATTN_DTYPE_BF16 && p->dtype != EXATTN_DTYPE_FP16)
+    return fail(EXATTN_ERR_DTYPE, "dtype %d is not supported: bf16 (0) or fp16 (1)", p->dtype);
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(EXATTN_ERR_HEAD_DIM, "head_dim %d is not supported: only 64 and 128", p->head_dim);
   if (p->heads_q < 1 || p->heads_kv < 1 || p->heads_q % p->heads_kv != 0)
@@ -177,6 +177,11 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace: [lse2 | Delta] fp32 in the lse layout, then the fp32 dQ accumulator
 // [rows_q, H, D] when the fused variant is selected.
+// The fused (atomic) backward is selected by variant 1 and exists for bf16 only.
+bool fused_backward(const exattn_problem* p) {
+  return get_bwd_variant() == 1 && p->dtype == EXATTN_DTYPE_BF16;
+}
+
 struct WsLayout {
   size_t lse2, delta, dq_acc, total;
 };
@@ -188,7 +193,7 @@ WsLayout ws_layout(const exattn_problem* p) {
   w.lse2 = 0;
   w.delta = w.lse2 + align256(nq * sizeof(float));
   w.dq_acc = w.delta + align256(nq * sizeof(float));
-  w.total = w.dq_acc + (get_bwd_variant() == 1 ? align256(nq * p->head_dim * sizeof(float)) : 0);
+  w.total = w.dq_acc + (fused_backward(p) ? align256(nq * p->head_dim * sizeof(float)) : 0);
   return w;
 }
 
@@ -291,7 +296,7 @@ exattn_status exattn_fwd(const exattn_problem* p, const void* q, const void* k, 
   hipError_t e;
   if (a.num_q_tiles > 0) {
     e = timed(KernelId::Fwd, s, [&] {
-      return launch_fwd(a, D, p->causal != 0, p->mask_kind, g.varlen, s);
+      return launch_fwd(a, D, p->dtype, p->causal != 0, p->mask_kind, g.varlen, s);
     });
     if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
   }
@@ -340,7 +345,7 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
   BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  const bool fused = get_bwd_variant() == 1;
+  const bool fused = fused_backward(p);
   a.dq_acc = fused ? reinterpret_cast<float*>(ws + w.dq_acc) : nullptr;
   a.lse2 = reinterpret_cast<float*>(ws + w.lse2);
   a.delta = reinterpret_cast<float*>(ws + w.delta);
@@ -387,12 +392,12 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
     if (e != hipSuccess) return hip_fail(e, "zero dk/dv");
     return EXATTN_OK;
   }
-  e = timed(KernelId::Delta, s, [&] { return launch_delta(a, D, g.varlen, s); });
+  e = timed(KernelId::Delta, s, [&] { return launch_delta(a, D, p->dtype, g.varlen, s); });
   if (e != hipSuccess) return hip_fail(e, "delta kernel launch");
   const bool causal = p->causal != 0;
   if (a.num_k_blocks > 0) {
     e = timed(fused ? KernelId::BwdFused : KernelId::BwdDkDv, s, [&] {
-      return launch_bwd(a, D, causal, p->mask_kind, g.varlen, fused, s);
+      return launch_bwd(a, D, p->dtype, causal, p->mask_kind, g.varlen, fused, s);
     });
     if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
   }
@@ -400,7 +405,7 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
     e = timed(KernelId::DqReduce, s, [&] { return launch_dq_reduce(a, D, s); });
     if (e != hipSuccess) return hip_fail(e, "dq reduce launch");
   } else {
-    e = timed(KernelId::BwdDq, s, [&] { return launch_bwd_dq(a, D, causal, p->mask_kind, g.varlen, s); });
+    e = timed(KernelId::BwdDq, s, [&] { return launch_bwd_dq(a, D, p->dtype, causal, p->mask_kind, g.varlen, s); });
     if (e != hipSuccess) return hip_fail(e, "dq kernel launch");
     if (g.varlen) {
       e = timed(KernelId::QTail, s, [&] { return launch_q_tail(a, D, s); });

@@ -35,8 +35,9 @@ using bool_c = std::integral_constant<bool, B>;
 // ----------------------------------------------------------------------------------------
 // 1. Delta / lse2 / dQ-accumulator clear. One group of D/8 lanes per (row, head).
 // ----------------------------------------------------------------------------------------
-template <int D, bool VARLEN>
+template <class E, int D, bool VARLEN>
 __global__ void __launch_bounds__(256) delta_kernel(BwdArgs a) {
+  using V8 = typename Ty<E>::v8;
   constexpr int LPR = D / 8;            // lanes per row
   constexpr int RPB = 256 / LPR;        // rows per block
   const int sub = threadIdx.x % LPR;
@@ -55,8 +56,8 @@ __global__ void __launch_bounds__(256) delta_kernel(BwdArgs a) {
     do_off = (int64_t)b * a.do_sb + (int64_t)s * a.do_ss + (int64_t)head * a.do_sh;
     st_idx = ((int64_t)b * a.H + head) * a.Sq + s;
   }
-  const bf16x8 o = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(a.out) + o_off + sub * 8);
-  const bf16x8 g = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(a.dout) + do_off + sub * 8);
+  const V8 o = *reinterpret_cast<const V8*>(reinterpret_cast<const E*>(a.out) + o_off + sub * 8);
+  const V8 g = *reinterpret_cast<const V8*>(reinterpret_cast<const E*>(a.dout) + do_off + sub * 8);
   float acc = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc += (float)o[i] * (float)g[i];
@@ -125,9 +126,11 @@ constexpr size_t bwd_smem_bytes() {
          4 * T::BM * sizeof(float);
 }
 
-template <int D, bool CAUSAL, int MASK, bool VARLEN, bool DQ>
+template <class E, int D, bool CAUSAL, int MASK, bool VARLEN, bool DQ>
 __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
   using T = BwdTile<D>;
+  using V8 = typename Ty<E>::v8;
+  using V4 = typename Ty<E>::v4;
   constexpr int kDqAtomics = 16;                 // buffer atomics per wave per dQ phase
   constexpr int RB = D * 2;                      // bytes per swizzled row
   constexpr int QBYTES = T::Q_ELEMS * 2;         // one Q or dO buffer
@@ -187,20 +190,20 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
 
   // The block's K (swizzled LDS, zero past the last key) and this pair's operand
   // fragments in registers: K for wave A (S = Q K^T), V for wave B (dP = dO V^T).
-  const bf16* K = reinterpret_cast<const bf16*>(a.k) + kb_off + (int64_t)g * a.k_sh +
+  const E* K = reinterpret_cast<const E*>(a.k) + kb_off + (int64_t)g * a.k_sh +
                   (int64_t)kb0 * a.k_ss;
-  const bf16* V = reinterpret_cast<const bf16*>(a.v) + vb_off + (int64_t)g * a.v_sh +
+  const E* V = reinterpret_cast<const E*>(a.v) + vb_off + (int64_t)g * a.v_sh +
                   (int64_t)kb0 * a.v_ss;
   const auto rk = make_rsrc(K, (uint32_t)((krows - 1) * a.k_ss + D) * 2u);
   const auto rv = make_rsrc(V, (uint32_t)((krows - 1) * a.v_ss + D) * 2u);
   if (DQ) copy_tile_to_lds<D, T::BN, T::NW>(k_b, rk, (int)a.k_ss, wave, lane);
-  bf16x8 kv[T::DS];
+  V8 kv[T::DS];
   {
     const auto r = role_a ? rk : rv;
     const int st = role_a ? (int)a.k_ss : (int)a.v_ss;
 #pragma unroll
     for (int s = 0; s < T::DS; ++s)
-      kv[s] = __builtin_bit_cast(bf16x8, buf_load16(r, (uint32_t)(kl_w * st + 16 * s + 8 * half) * 2u));
+      kv[s] = __builtin_bit_cast(V8, buf_load16(r, (uint32_t)(kl_w * st + 16 * s + 8 * half) * 2u));
   }
 
   // ---- per-lane LDS base addresses; everything else is an immediate offset ----------------
@@ -270,9 +273,9 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
   auto load_q = [&](const TilePos& tp, int buf) {
     const int head = tp.head, qt0 = tp.q0;
     const int rows = min(T::BM, Sq - qt0);
-    const bf16* Qp = reinterpret_cast<const bf16*>(a.q) + qb_off + (int64_t)head * a.q_sh +
+    const E* Qp = reinterpret_cast<const E*>(a.q) + qb_off + (int64_t)head * a.q_sh +
                      (int64_t)qt0 * a.q_ss;
-    const bf16* Dp = reinterpret_cast<const bf16*>(a.dout) + dob_off + (int64_t)head * a.do_sh +
+    const E* Dp = reinterpret_cast<const E*>(a.dout) + dob_off + (int64_t)head * a.do_sh +
                      (int64_t)qt0 * a.do_ss;
     copy_tile_to_lds<D, T::BM, T::NW>(q_b + buf * QBYTES,
                                      make_rsrc(Qp, (uint32_t)((rows - 1) * a.q_ss + D) * 2u),
@@ -365,7 +368,7 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
       for (int ds = 0; ds < T::DS; ++ds) {
 #pragma unroll
         for (int qb = 0; qb < T::QB; ++qb)
-          sp[qb] = mfma32(lds_at<bf16x8>(aq[ds] + po, QO + qb * 32 * RB), kv[ds], sp[qb]);
+          sp[qb] = mfma32(lds_at<V8>(aq[ds] + po, QO + qb * 32 * RB), kv[ds], sp[qb]);
       }
     }
     if (role_a) {
@@ -396,20 +399,20 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
         if (DQ) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            *reinterpret_cast<bf16*>(dsw + (qb * 32 + 8 * (r >> 2) + (r & 3)) * T::SLD * 2) =
-                (bf16)sp[qb][r];
+            *reinterpret_cast<E*>(dsw + (qb * 32 + 8 * (r >> 2) + (r & 3)) * T::SLD * 2) =
+                (E)sp[qb][r];
         }
       }
     }
 #pragma unroll
     for (int kk = 0; kk < T::BM / 16; ++kk) {
       const int qb = kk >> 1, hs = (kk & 1) * 8;
-      const bf16x8 pa = cvt8(sp[qb][hs + 0], sp[qb][hs + 1], sp[qb][hs + 2], sp[qb][hs + 3],
+      const V8 pa = cvt8<V8>(sp[qb][hs + 0], sp[qb][hs + 1], sp[qb][hs + 2], sp[qb][hs + 3],
                              sp[qb][hs + 4], sp[qb][hs + 5], sp[qb][hs + 6], sp[qb][hs + 7]);
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) {
         const int o = QO + 16 * kk * RB;
-        const bf16x8 bv = cat44(tr_at(tq[db][0], o), tr_at(tq[db][1], o));
+        const V8 bv = cat44(tr_at<V4>(tq[db][0], o), tr_at<V4>(tq[db][1], o));
         acc[db] = mfma32(pa, bv, acc[db]);
       }
     }
@@ -431,9 +434,9 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
       f32x16 dq = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < T::BN / 16; ++kk) {
-        const bf16x8 sv = lds_at<bf16x8>(dsr, (qb * 32 * T::SLD + kk * 16) * 2);
+        const V8 sv = lds_at<V8>(dsr, (qb * 32 * T::SLD + kk * 16) * 2);
         const int o = 16 * kk * RB;
-        const bf16x8 kvv = cat44(tr_at(tk[0], o), tr_at(tk[1], o));
+        const V8 kvv = cat44(tr_at<V4>(tk[0], o), tr_at<V4>(tk[1], o));
         dq = mfma32(sv, kvv, dq);
       }
 #pragma unroll
@@ -458,14 +461,14 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
   const float sc = role_a ? 1.f : a.scale;
   const int64_t kv_off = ((krow0 + kb0) * a.Hkv + g) * D;
   const uint32_t kv_bytes = (uint32_t)((krows - 1) * a.Hkv * D + D) * 2u;
-  const auto rout = make_rsrc(reinterpret_cast<bf16*>(role_a ? a.dv : a.dk) + kv_off, kv_bytes);
+  const auto rout = make_rsrc(reinterpret_cast<E*>(role_a ? a.dv : a.dk) + kv_off, kv_bytes);
 #pragma unroll
   for (int db = 0; db < T::DB; ++db) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = kg * 32 + acc_row(r, half);
       const int off = (key * a.Hkv * D + db * 32 + l32) * 2;
-      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)(acc[db][r] * sc)),
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (E)(acc[db][r] * sc)),
                                             rout, off, 0, 0);
     }
   }
@@ -497,9 +500,11 @@ struct DqTile {
   static_assert((BN * D / 8) % (64 * NW) == 0, "even copy split");
 };
 
-template <int D, bool CAUSAL, int MASK, bool VARLEN>
+template <class E, int D, bool CAUSAL, int MASK, bool VARLEN>
 __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
   using T = DqTile<D>;
+  using V8 = typename Ty<E>::v8;
+  using V4 = typename Ty<E>::v4;
   constexpr int RB = D * 2;
   constexpr int V_OFF = 2 * T::TBYTES;           // V buffers follow the two K buffers
   __shared__ __attribute__((aligned(16))) unsigned char smem[4 * T::TBYTES];
@@ -540,27 +545,27 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
   }
   const int qt0 = qtile * T::BM;
   if (qt0 >= Sq) return;
-  const bf16* K = reinterpret_cast<const bf16*>(a.k) + k_base;
-  const bf16* V = reinterpret_cast<const bf16*>(a.v) + v_base;
+  const E* K = reinterpret_cast<const E*>(a.k) + k_base;
+  const E* V = reinterpret_cast<const E*>(a.v) + v_base;
 
   // This lane's query row: Q and dO fragments, lse2 and Delta (zero / +inf past the end).
   const int qw0 = qt0 + wave * 32;
   const int qi = qw0 + l32;
-  bf16x8 qf[T::DS], df[T::DS];
+  V8 qf[T::DS], df[T::DS];
   float l2 = INFINITY, dl = 0.f;
   if (qi < Sq) {
-    const bf16* qr = reinterpret_cast<const bf16*>(a.q) + q_base + (int64_t)qi * a.q_ss + 8 * half;
-    const bf16* dr = reinterpret_cast<const bf16*>(a.dout) + do_base + (int64_t)qi * a.do_ss + 8 * half;
+    const E* qr = reinterpret_cast<const E*>(a.q) + q_base + (int64_t)qi * a.q_ss + 8 * half;
+    const E* dr = reinterpret_cast<const E*>(a.dout) + do_base + (int64_t)qi * a.do_ss + 8 * half;
 #pragma unroll
     for (int s = 0; s < T::DS; ++s) {
-      qf[s] = *reinterpret_cast<const bf16x8*>(qr + 16 * s);
-      df[s] = *reinterpret_cast<const bf16x8*>(dr + 16 * s);
+      qf[s] = *reinterpret_cast<const V8*>(qr + 16 * s);
+      df[s] = *reinterpret_cast<const V8*>(dr + 16 * s);
     }
     l2 = a.lse2[st_base + qi];
     dl = a.delta[st_base + qi];
   } else {
 #pragma unroll
-    for (int s = 0; s < T::DS; ++s) qf[s] = df[s] = bf16x8{};
+    for (int s = 0; s < T::DS; ++s) qf[s] = df[s] = V8{};
   }
 
   const int kend = CAUSAL ? min(Sk, qt0 + T::BM) : Sk;
@@ -622,8 +627,8 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
     for (int ds = 0; ds < T::DS; ++ds) {
 #pragma unroll
       for (int kb = 0; kb < T::KB; ++kb) {
-        s[kb] = mfma32(lds_at<bf16x8>(ar[ds], KO + kb * 32 * RB), qf[ds], s[kb]);
-        dp[kb] = mfma32(lds_at<bf16x8>(ar[ds], V_OFF + KO + kb * 32 * RB), df[ds], dp[kb]);
+        s[kb] = mfma32(lds_at<V8>(ar[ds], KO + kb * 32 * RB), qf[ds], s[kb]);
+        dp[kb] = mfma32(lds_at<V8>(ar[ds], V_OFF + KO + kb * 32 * RB), df[ds], dp[kb]);
       }
     }
     const int kb0 = t * T::BN;
@@ -659,12 +664,12 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int kk = 0; kk < T::BN / 16; ++kk) {
       const int kb = kk >> 1, hs = (kk & 1) * 8;
-      const bf16x8 sb = cvt8(dp[kb][hs + 0], dp[kb][hs + 1], dp[kb][hs + 2], dp[kb][hs + 3],
+      const V8 sb = cvt8<V8>(dp[kb][hs + 0], dp[kb][hs + 1], dp[kb][hs + 2], dp[kb][hs + 3],
                              dp[kb][hs + 4], dp[kb][hs + 5], dp[kb][hs + 6], dp[kb][hs + 7]);
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) {
         const int o = KO + 16 * kk * RB;
-        const bf16x8 ka = cat44(tr_at(tk[db][0], o), tr_at(tk[db][1], o));
+        const V8 ka = cat44(tr_at<V4>(tk[db][0], o), tr_at<V4>(tk[db][1], o));
         dq[db] = mfma32(ka, sb, dq[db]);
       }
     }
@@ -691,21 +696,23 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
 
   // Epilogue: dq = bf16(dQ * scale), contiguous [rows_q, H, D], through this wave's slice
   // of LDS (free after the last barrier); rows past Sq are not written.
-  bf16* dqw = reinterpret_cast<bf16*>(a.dq) + ((qrow0 + qw0) * a.H + head) * D;
+  E* dqw = reinterpret_cast<E*>(a.dq) + ((qrow0 + qw0) * a.H + head) * D;
   static_assert(T::NW * 32 * D * 2 <= 4 * T::TBYTES, "epilogue staging fits the tile buffers");
-  wave_store_rows<D>(smem + wave * 32 * D * 2, dq, a.scale, dqw, (int64_t)a.H * D, Sq - qw0, lane);
+  wave_store_rows<D, E>(smem + wave * 32 * D * 2, dq, a.scale, dqw, (int64_t)a.H * D, Sq - qw0, lane);
 }
 
 // ----------------------------------------------------------------------------------------
 // 3. dq = bf16(dq_acc * scale), 8 elements per thread.
 // ----------------------------------------------------------------------------------------
+template <class E>
 __global__ void __launch_bounds__(256) dq_reduce_kernel(BwdArgs a, int64_t n8) {
+  using V8 = typename Ty<E>::v8;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n8) return;
   const f32x4* src = reinterpret_cast<const f32x4*>(a.dq_acc) + 2 * i;
   const f32x4 x0 = src[0], x1 = src[1];
   const float sc = a.scale;
-  reinterpret_cast<bf16x8*>(a.dq)[i] = cvt8(x0[0] * sc, x0[1] * sc, x0[2] * sc, x0[3] * sc,
+  reinterpret_cast<V8*>(a.dq)[i] = cvt8<V8>(x0[0] * sc, x0[1] * sc, x0[2] * sc, x0[3] * sc,
                                             x1[0] * sc, x1[1] * sc, x1[2] * sc, x1[3] * sc);
 }
 
@@ -756,31 +763,38 @@ static int g_bwd_variant = 0;
 void set_bwd_variant(int v) { g_bwd_variant = (v == 1) ? 1 : 0; }
 int get_bwd_variant() { return g_bwd_variant; }
 
-hipError_t launch_delta(const BwdArgs& a, int head_dim, bool varlen, hipStream_t s) {
+template <class E>
+static hipError_t launch_delta_e(const BwdArgs& a, int head_dim, bool varlen, hipStream_t s) {
   const int64_t nrows = (int64_t)a.rows_q * a.H;
   if (nrows <= 0) return hipSuccess;
   const int rpb = 256 / (head_dim / 8);
   dim3 grid((unsigned)((nrows + rpb - 1) / rpb)), block(256);
   if (head_dim == 64) {
-    if (varlen) hipLaunchKernelGGL((delta_kernel<64, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((delta_kernel<64, false>), grid, block, 0, s, a);
+    if (varlen) hipLaunchKernelGGL((delta_kernel<E, 64, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((delta_kernel<E, 64, false>), grid, block, 0, s, a);
   } else {
-    if (varlen) hipLaunchKernelGGL((delta_kernel<128, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((delta_kernel<128, false>), grid, block, 0, s, a);
+    if (varlen) hipLaunchKernelGGL((delta_kernel<E, 128, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((delta_kernel<E, 128, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
 
-template <int D>
-static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, int mask, bool varlen, bool fused,
-                               hipStream_t s) {
+hipError_t launch_delta(const BwdArgs& a, int head_dim, int dtype, bool varlen, hipStream_t s) {
+  if (dtype == kDtypeF16) return launch_delta_e<f16>(a, head_dim, varlen, s);
+  return launch_delta_e<bf16>(a, head_dim, varlen, s);
+}
+
+// The fused (atomic) kernel is compiled for bf16 only; fp16 problems always take the
+// split backward.
+template <class E, int D, bool FUSED>
+static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, int mask, bool varlen, hipStream_t s) {
   const int64_t nblk = (int64_t)a.num_units * a.Hkv * a.num_k_blocks;
   if (nblk <= 0) return hipSuccess;
   dim3 grid((unsigned)nblk), block(512);
+  constexpr int smem = (int)bwd_smem_bytes<D, FUSED>();
 #define EXATTN_BWD(C, M, V)                                                                    \
   do {                                                                                         \
-    auto kfn = fused ? bwd_kernel<D, C, M, V, true> : bwd_kernel<D, C, M, V, false>;           \
-    const int smem = (int)(fused ? bwd_smem_bytes<D, true>() : bwd_smem_bytes<D, false>());   \
+    auto kfn = bwd_kernel<E, D, C, M, V, FUSED>;                                               \
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                     \
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);      \
     if (e != hipSuccess) return e;                                                             \
@@ -802,19 +816,27 @@ static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, int mask, bool var
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool causal, int mask, bool varlen,
-                      bool fused, hipStream_t s) {
-  if (head_dim == 64) return launch_bwd_d<64>(a, causal, mask, varlen, fused, s);
-  return launch_bwd_d<128>(a, causal, mask, varlen, fused, s);
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, int dtype, bool causal, int mask,
+                      bool varlen, bool fused, hipStream_t s) {
+  if (dtype == kDtypeF16) {
+    if (head_dim == 64) return launch_bwd_d<f16, 64, false>(a, causal, mask, varlen, s);
+    return launch_bwd_d<f16, 128, false>(a, causal, mask, varlen, s);
+  }
+  if (head_dim == 64) {
+    if (fused) return launch_bwd_d<bf16, 64, true>(a, causal, mask, varlen, s);
+    return launch_bwd_d<bf16, 64, false>(a, causal, mask, varlen, s);
+  }
+  if (fused) return launch_bwd_d<bf16, 128, true>(a, causal, mask, varlen, s);
+  return launch_bwd_d<bf16, 128, false>(a, causal, mask, varlen, s);
 }
 
-template <int D>
+template <class E, int D>
 static hipError_t launch_bwd_dq_d(const BwdArgs& a, bool causal, int mask, bool varlen,
                                   hipStream_t s) {
   const int64_t nblk = (int64_t)a.num_units * a.H * a.num_q_blocks;
   if (nblk <= 0) return hipSuccess;
   dim3 grid((unsigned)nblk), block(512);
-#define EXATTN_DQ(C, M, V) hipLaunchKernelGGL((bwd_dq_kernel<D, C, M, V>), grid, block, 0, s, a)
+#define EXATTN_DQ(C, M, V) hipLaunchKernelGGL((bwd_dq_kernel<E, D, C, M, V>), grid, block, 0, s, a)
   if (varlen) {
     if (causal) EXATTN_DQ(true, kMaskNone, true);
     else EXATTN_DQ(false, kMaskNone, true);
@@ -831,10 +853,14 @@ static hipError_t launch_bwd_dq_d(const BwdArgs& a, bool causal, int mask, bool 
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, bool causal, int mask, bool varlen,
-                         hipStream_t s) {
-  if (head_dim == 64) return launch_bwd_dq_d<64>(a, causal, mask, varlen, s);
-  return launch_bwd_dq_d<128>(a, causal, mask, varlen, s);
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int dtype, bool causal, int mask,
+                         bool varlen, hipStream_t s) {
+  if (dtype == kDtypeF16) {
+    if (head_dim == 64) return launch_bwd_dq_d<f16, 64>(a, causal, mask, varlen, s);
+    return launch_bwd_dq_d<f16, 128>(a, causal, mask, varlen, s);
+  }
+  if (head_dim == 64) return launch_bwd_dq_d<bf16, 64>(a, causal, mask, varlen, s);
+  return launch_bwd_dq_d<bf16, 128>(a, causal, mask, varlen, s);
 }
 
 int bwd_dq_block_m(int head_dim) { return DqTile<128>::BM; }
@@ -843,7 +869,7 @@ hipError_t launch_dq_reduce(const BwdArgs& a, int head_dim, hipStream_t s) {
   const int64_t n8 = (int64_t)a.rows_q * a.H * head_dim / 8;
   if (n8 <= 0) return hipSuccess;
   dim3 grid((unsigned)((n8 + 255) / 256)), block(256);
-  hipLaunchKernelGGL(dq_reduce_kernel, grid, block, 0, s, a, n8);
+  hipLaunchKernelGGL(dq_reduce_kernel<bf16>, grid, block, 0, s, a, n8);
   return hipGetLastError();
 }
 

@@ -9,6 +9,9 @@ namespace exattn {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -18,6 +21,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 enum MaskMode { kMaskNone = 0, kMaskBool = 1, kMaskAdd = 2 };
+enum DtypeCode { kDtypeBf16 = 0, kDtypeF16 = 1 };   // values of exattn_dtype
 
 // D[32x32] += A[32x16] * B[16x32] on one wavefront, bf16 in, fp32 accumulate.
 // Operand layout: lane l holds row (A) or column (B) l % 32 and eight k-slots for k-half
@@ -27,18 +31,41 @@ enum MaskMode { kMaskNone = 0, kMaskBool = 1, kMaskAdd = 2 };
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// The two 16-bit input formats share every data path; only the MFMA instruction (chosen
+// by overload) and the rounding of fp32 results differ.
+template <class E>
+struct Ty;
+template <>
+struct Ty<bf16> {
+  typedef bf16x8 v8;
+  typedef bf16x4 v4;
+};
+template <>
+struct Ty<f16> {
+  typedef f16x8 v8;
+  typedef f16x4 v4;
+};
 
 __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ bf16x8 cvt8(float a0, float a1, float a2, float a3, float a4,
-                                       float a5, float a6, float a7) {
+// Eight fp32 values rounded (to nearest even) to one 16-byte fragment of the input format.
+template <class V8 = bf16x8>
+__device__ __forceinline__ V8 cvt8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                   float a6, float a7) {
   f32x8 f = {a0, a1, a2, a3, a4, a5, a6, a7};
-  return __builtin_convertvector(f, bf16x8);
+  return __builtin_convertvector(f, V8);
 }
 
 __device__ __forceinline__ bf16x8 cat44(bf16x4 lo, bf16x4 hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f16x8 cat44(f16x4 lo, f16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -56,11 +83,12 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 // Transposed LDS read (ds_read_b64_tr_b16). Within each 16-lane group, if lane j points at
 // row k0 + j/4, columns n0 + 4*(j%4) .. +3 of a row-major bf16 tile, lane i receives
 // column n0 + i, rows k0 .. k0+3: an MFMA operand fragment read from the other-major layout.
-__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+template <class V4 = bf16x4>
+__device__ __forceinline__ V4 lds_read_tr4(const void* p) {
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(const_cast<bf16*>(p)));
-  return __builtin_bit_cast(bf16x4, v);
+      (__attribute__((address_space(3))) s16x4*)(const_cast<void*>(p)));
+  return __builtin_bit_cast(V4, v);
 }
 
 // Map a hardware block index to a logical one so that consecutive logical blocks run on
@@ -134,8 +162,9 @@ template <class V>
 __device__ __forceinline__ V lds_at(const unsigned char* base, int imm) {
   return *reinterpret_cast<const V*>(base + imm);
 }
-__device__ __forceinline__ bf16x4 tr_at(const unsigned char* base, int imm) {
-  return lds_read_tr4(reinterpret_cast<const bf16*>(base + imm));
+template <class V4 = bf16x4>
+__device__ __forceinline__ V4 tr_at(const unsigned char* base, int imm) {
+  return lds_read_tr4<V4>(base + imm);
 }
 
 // Store a wave's 32 x D result block as bf16 rows, coalesced. `acc[db]` holds the block in
@@ -145,10 +174,11 @@ __device__ __forceinline__ bf16x4 tr_at(const unsigned char* base, int imm) {
 // 16-byte reads avoid bank conflicts), then each lane stores 16 contiguous bytes: every
 // store instruction covers whole rows. Rows r >= nrows are not written. The caller makes
 // sure no other wave uses `buf` meanwhile.
-template <int D>
+template <int D, class E>
 __device__ __forceinline__ void wave_store_rows(unsigned char* buf, const f32x16 (&acc)[D / 32],
-                                                float scale, bf16* dst, int64_t row_stride,
+                                                float scale, E* dst, int64_t row_stride,
                                                 int nrows, int lane) {
+  typedef typename Ty<E>::v4 V4;
   constexpr int RB = D * 2;
   constexpr int CPR = D / 8;                     // 16-byte chunks per row
   const int half = lane >> 5, l32 = lane & 31;
@@ -159,8 +189,8 @@ __device__ __forceinline__ void wave_store_rows(unsigned char* buf, const f32x16
       const int c8 = db * 8 + 2 * rg + half;     // 8-byte chunk of columns 4*c8 .. 4*c8+3
       f32x4 v = {acc[db][4 * rg] * scale, acc[db][4 * rg + 1] * scale, acc[db][4 * rg + 2] * scale,
                  acc[db][4 * rg + 3] * scale};
-      *reinterpret_cast<bf16x4*>(buf + l32 * RB + 16 * ((c8 >> 1) ^ (l32 & (CPR - 1))) + 8 * (c8 & 1)) =
-          __builtin_convertvector(v, bf16x4);
+      *reinterpret_cast<V4*>(buf + l32 * RB + 16 * ((c8 >> 1) ^ (l32 & (CPR - 1))) + 8 * (c8 & 1)) =
+          __builtin_convertvector(v, V4);
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

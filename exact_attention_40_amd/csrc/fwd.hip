@@ -12,7 +12,7 @@
 //   32 query rows and keeps their Q fragments in registers; K and V tiles of 64 keys are
 //   copied straight from global memory into XOR-swizzled LDS (buffer loads with an LDS
 //   destination, zero past the last key), K one tile further ahead than V.
-// S^T = K Q^T is computed with 32x32x16 bf16 MFMAs so that a lane's accumulator holds one
+// S^T = K Q^T is computed with 32x32x16 MFMAs (bf16 or fp16 inputs) so that a lane's accumulator holds one
 // query column: row statistics are per lane plus one exchange with the partner lane
 // (l ^ 32), the output rescale is a per-lane scalar, and the exponentiated scores feed
 // the O^T += V^T P^T MFMA as its B operand straight from registers. V stays row-major in
@@ -61,10 +61,12 @@ using int_c = std::integral_constant<int, I>;
 
 // QB = 1: two waves per SIMD (8 waves x 32 rows); QB = 2: one wave per SIMD (4 waves x 64
 // rows), which halves the LDS reads per MFMA and relies on the in-stream interleave alone.
-template <int D, int NW, int QB, bool CAUSAL, int MASK, bool VARLEN, bool LAZY>
+template <class E, int D, int NW, int QB, bool CAUSAL, int MASK, bool VARLEN, bool LAZY>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(QB == 1 ? 2 : 1)))
 fwd_kernel(FwdArgs a) {
   using T = FwdTile<D, NW, QB>;
+  using V8 = typename Ty<E>::v8;
+  using V4 = typename Ty<E>::v4;
   constexpr int RB = T::RB;
   constexpr int V_OFF = 2 * T::TBYTES;           // V buffers follow the two K buffers
   __shared__ __attribute__((aligned(16))) unsigned char smem[4 * T::TBYTES];
@@ -103,9 +105,9 @@ fwd_kernel(FwdArgs a) {
   const int qt0 = qtile * T::BM;
   if (qt0 >= Sq) return;
 
-  const bf16* Q = reinterpret_cast<const bf16*>(a.q) + q_base;
-  const bf16* K = reinterpret_cast<const bf16*>(a.k) + k_base;
-  const bf16* V = reinterpret_cast<const bf16*>(a.v) + v_base;
+  const E* Q = reinterpret_cast<const E*>(a.q) + q_base;
+  const E* K = reinterpret_cast<const E*>(a.k) + k_base;
+  const E* V = reinterpret_cast<const E*>(a.v) + v_base;
 
   // A negative scale is folded into the sign of Q: (-q).k * |c| equals q.k * c exactly
   // (negation commutes with every rounding), so the row max is always a max.
@@ -115,18 +117,18 @@ fwd_kernel(FwdArgs a) {
 
   // Q fragments of this lane's query rows, B-operand layout (column = query, k-slots = d).
   int qi[QB];
-  bf16x8 qf[QB][T::DS];
+  V8 qf[QB][T::DS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     qi[qb] = qt0 + (wave * QB + qb) * 32 + l32;
     if (qi[qb] < Sq) {
-      const bf16* row = Q + (int64_t)qi[qb] * a.q_ss + 8 * half;
+      const E* row = Q + (int64_t)qi[qb] * a.q_ss + 8 * half;
 #pragma unroll
       for (int s = 0; s < T::DS; ++s)
-        qf[qb][s] = __builtin_bit_cast(bf16x8, ldg16(row + 16 * s) ^ u32x4{qsign, qsign, qsign, qsign});
+        qf[qb][s] = __builtin_bit_cast(V8, ldg16(row + 16 * s) ^ u32x4{qsign, qsign, qsign, qsign});
     } else {
 #pragma unroll
-      for (int s = 0; s < T::DS; ++s) qf[qb][s] = bf16x8{};
+      for (int s = 0; s < T::DS; ++s) qf[qb][s] = V8{};
     }
   }
 
@@ -288,10 +290,10 @@ fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < T::KB; ++kb) nxt[qb][kb] = f32x16{};
     }
-    auto kfrag = [&](int f) { return lds_at<bf16x8>(ar[f / T::KB], KO + (f % T::KB) * 32 * RB); };
-    auto vfrag = [&](int kk, int db, int sec) { return tr_at(tv[db][sec], VB + 16 * kk * RB); };
-    bf16x8 kf[3] = {kfrag(0), kfrag(1), kfrag(2)};
-    bf16x4 vt[2][T::DB][2];
+    auto kfrag = [&](int f) { return lds_at<V8>(ar[f / T::KB], KO + (f % T::KB) * 32 * RB); };
+    auto vfrag = [&](int kk, int db, int sec) { return tr_at<V4>(tv[db][sec], VB + 16 * kk * RB); };
+    V8 kf[3] = {kfrag(0), kfrag(1), kfrag(2)};
+    V4 vt[2][T::DB][2];
 #pragma unroll
     for (int i = 0; i < QSTEPS; ++i) {
       const int f = i / QB, qb = i % QB;
@@ -336,10 +338,10 @@ fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int kb = kk >> 1, hs = (kk & 1) * 8;
-      bf16x8 pf[QB];
+      V8 pf[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-        pf[qb] = cvt8(cur[qb][kb][hs + 0], cur[qb][kb][hs + 1], cur[qb][kb][hs + 2],
+        pf[qb] = cvt8<V8>(cur[qb][kb][hs + 0], cur[qb][kb][hs + 1], cur[qb][kb][hs + 2],
                       cur[qb][kb][hs + 3], cur[qb][kb][hs + 4], cur[qb][kb][hs + 5],
                       cur[qb][kb][hs + 6], cur[qb][kb][hs + 7]);
 #pragma unroll
@@ -399,7 +401,7 @@ fwd_kernel(FwdArgs a) {
     for (int ds = 0; ds < T::DS; ++ds) {
 #pragma unroll
       for (int kb = 0; kb < T::KB; ++kb) {
-        const bf16x8 kfr = lds_at<bf16x8>(ar[ds], kb * 32 * RB);
+        const V8 kfr = lds_at<V8>(ar[ds], kb * 32 * RB);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) sa[qb][kb] = mfma32(kfr, qf[qb][ds], sa[qb][kb]);
       }
@@ -446,16 +448,16 @@ fwd_kernel(FwdArgs a) {
     if (t + 1 < ntiles) iteration(t + 1, sb, sa, int_c<1>{}, Tr{}, Tr{});
   }
 
-  // Epilogue: normalise, write out (bf16, RNE) through this wave's slice of LDS (every wave
+  // Epilogue: normalise, write out (input format, RNE) through this wave's slice of LDS (every wave
   // has passed the last barrier, so the K/V buffers are free) and lse (natural log).
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l = l_run[qb] + wave_xor32(l_run[qb]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int r0 = qt0 + (wave * QB + qb) * 32;
-    bf16* orow = reinterpret_cast<bf16*>(a.out) + o_base + (int64_t)r0 * a.o_ss;
+    E* orow = reinterpret_cast<E*>(a.out) + o_base + (int64_t)r0 * a.o_ss;
     static_assert(NW * QB * 32 * D * 2 <= 4 * T::TBYTES, "epilogue staging fits the tile buffers");
-    wave_store_rows<D>(smem + (wave * QB + qb) * 32 * D * 2, o[qb], inv, orow, a.o_ss,
+    wave_store_rows<D, E>(smem + (wave * QB + qb) * 32 * D * 2, o[qb], inv, orow, a.o_ss,
                        Sq - r0, lane);
     if (qi[qb] < Sq && half == 0) {
       const float mu = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
@@ -471,37 +473,35 @@ __global__ void __launch_bounds__(256) fwd_tail_kernel(FwdArgs a) {
   if (idx >= (int64_t)a.Sq * a.H) return;
   const int row = (int)(idx / a.H), head = (int)(idx % a.H);
   if (row < a.cu_q[a.num_units]) return;
-  bf16* o = reinterpret_cast<bf16*>(a.out) + (int64_t)row * a.o_ss + (int64_t)head * a.o_sh;
+  uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (int64_t)row * a.o_ss + (int64_t)head * a.o_sh;
 #pragma unroll
   for (int d = 0; d < D; d += 8) *reinterpret_cast<u32x4*>(o + d) = u32x4{0, 0, 0, 0};
   a.lse[(int64_t)head * a.lse_row + row] = -INFINITY;
 }
 
 // Variants: 0 = 8 waves x 32 rows, lazy rescale (default); 1 = 8 waves x 32 rows, eager
-// rescale; 2 = 4 waves x 64 rows (lazy), one wave per SIMD. Variant 2 is compiled for
-// head_dim 128 without a mask or cu_seqlens; other problems use variant 0.
+// rescale; 2 = 4 waves x 64 rows (lazy), one wave per SIMD. Variant 2 is compiled for bf16,
+// head_dim 128, without a mask or cu_seqlens; other problems use variant 0.
 static int g_fwd_variant = 0;
 
 void set_fwd_variant(int v) { g_fwd_variant = (v >= 0 && v <= 2) ? v : 0; }
 int get_fwd_variant() { return g_fwd_variant; }
 
-static int effective_variant(int head_dim, int mask, bool varlen) {
+static int effective_variant(int head_dim, int dtype, int mask, bool varlen) {
   const int v = g_fwd_variant;
-  if (v == 2 && (head_dim != 128 || mask != kMaskNone || varlen)) return 0;
+  if (v == 2 && (head_dim != 128 || dtype != kDtypeBf16 || mask != kMaskNone || varlen)) return 0;
   return v;
 }
 
-int fwd_block_m(int head_dim, int mask, bool varlen) {
-  return 256;
-}
+int fwd_block_m(int head_dim, int mask, bool varlen) { return 256; }
 
-template <int D, int NW, int QB, bool LAZY>
+template <class E, int D, int NW, int QB, bool LAZY>
 static hipError_t launch_fwd_d(const FwdArgs& a, bool causal, int mask, bool varlen, hipStream_t s) {
   const int64_t nblk = (int64_t)a.num_units * a.H * a.num_q_tiles;
   if (nblk <= 0) return hipSuccess;
   dim3 grid((unsigned)nblk), block(64 * NW);
 #define EXATTN_FWD(C, M, V) \
-  hipLaunchKernelGGL((fwd_kernel<D, NW, QB, C, M, V, LAZY>), grid, block, 0, s, a)
+  hipLaunchKernelGGL((fwd_kernel<E, D, NW, QB, C, M, V, LAZY>), grid, block, 0, s, a)
   if (varlen) {
     if (causal) EXATTN_FWD(true, kMaskNone, true);
     else EXATTN_FWD(false, kMaskNone, true);
@@ -524,22 +524,29 @@ static hipError_t launch_fwd_plain128(const FwdArgs& a, bool causal, hipStream_t
   if (nblk <= 0) return hipSuccess;
   dim3 grid((unsigned)nblk), block(64 * NW);
   if (causal)
-    hipLaunchKernelGGL((fwd_kernel<128, NW, QB, true, kMaskNone, false, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((fwd_kernel<bf16, 128, NW, QB, true, kMaskNone, false, true>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<128, NW, QB, false, kMaskNone, false, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((fwd_kernel<bf16, 128, NW, QB, false, kMaskNone, false, true>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool causal, int mask, bool varlen,
-                      hipStream_t s) {
-  const int v = effective_variant(head_dim, mask, varlen);
+template <class E>
+static hipError_t launch_fwd_e(const FwdArgs& a, int head_dim, int v, bool causal, int mask,
+                               bool varlen, hipStream_t s) {
   if (head_dim == 64) {
-    if (v == 1) return launch_fwd_d<64, 8, 1, false>(a, causal, mask, varlen, s);
-    return launch_fwd_d<64, 8, 1, true>(a, causal, mask, varlen, s);
+    if (v == 1) return launch_fwd_d<E, 64, 8, 1, false>(a, causal, mask, varlen, s);
+    return launch_fwd_d<E, 64, 8, 1, true>(a, causal, mask, varlen, s);
   }
-  if (v == 1) return launch_fwd_d<128, 8, 1, false>(a, causal, mask, varlen, s);
+  if (v == 1) return launch_fwd_d<E, 128, 8, 1, false>(a, causal, mask, varlen, s);
+  return launch_fwd_d<E, 128, 8, 1, true>(a, causal, mask, varlen, s);
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, int dtype, bool causal, int mask,
+                      bool varlen, hipStream_t s) {
+  const int v = effective_variant(head_dim, dtype, mask, varlen);
   if (v == 2) return launch_fwd_plain128<4, 2>(a, causal, s);
-  return launch_fwd_d<128, 8, 1, true>(a, causal, mask, varlen, s);
+  if (dtype == kDtypeF16) return launch_fwd_e<f16>(a, head_dim, v, causal, mask, varlen, s);
+  return launch_fwd_e<bf16>(a, head_dim, v, causal, mask, varlen, s);
 }
 
 hipError_t launch_fwd_tail(const FwdArgs& a, int head_dim, hipStream_t s) {

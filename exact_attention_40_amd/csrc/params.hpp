@@ -68,14 +68,14 @@ enum class KernelId : int {
 const char* kernel_name(KernelId id);
 
 // Launchers return hipGetLastError() after the launch. `variant` selects the tiling.
-hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool causal, int mask_mode, bool varlen,
-                      hipStream_t s);
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, int dtype, bool causal, int mask_mode,
+                      bool varlen, hipStream_t s);
 hipError_t launch_fwd_tail(const FwdArgs& a, int head_dim, hipStream_t s);
-hipError_t launch_delta(const BwdArgs& a, int head_dim, bool varlen, hipStream_t s);
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool causal, int mask_mode, bool varlen,
-                      bool fused_dq, hipStream_t s);
-hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, bool causal, int mask_mode, bool varlen,
-                         hipStream_t s);
+hipError_t launch_delta(const BwdArgs& a, int head_dim, int dtype, bool varlen, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, int dtype, bool causal, int mask_mode,
+                      bool varlen, bool fused_dq, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int dtype, bool causal, int mask_mode,
+                         bool varlen, hipStream_t s);
 hipError_t launch_q_tail(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_dq_reduce(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_kv_tail(const BwdArgs& a, int head_dim, hipStream_t s);

@@ -72,24 +72,27 @@ def _rng(seed):
     return np.random.Generator(np.random.PCG64(seed))
 
 
-def _normal_bf16(rng, shape, mult=1.0):
+def _normal(rng, shape, mult=1.0, dtype=torch.bfloat16):
+    """float32 standard normals (times mult) rounded to the 16-bit input format."""
     x = rng.standard_normal(size=shape, dtype=np.float32)
     if mult != 1.0:
         x *= np.float32(mult)
-    return torch.from_numpy(x).to(torch.bfloat16)
+    return torch.from_numpy(x).to(dtype)
 
 
 def dense(B, Sq, Sk, H, Hkv, D, seed, *, causal=False, k_mult=1.0, dout_ones=False,
-          name="dense"):
-    """q, v, dout ~ N(0,1), k ~ N(0,1) * k_mult, all bf16, BSHD contiguous."""
+          name="dense", dtype=torch.bfloat16):
+    """q, v, dout ~ N(0,1), k ~ N(0,1) * k_mult, all in `dtype` (bf16 or fp16), BSHD
+    contiguous."""
     rng = _rng(seed)
-    q = _normal_bf16(rng, (B, Sq, H, D))
-    k = _normal_bf16(rng, (B, Sk, Hkv, D), k_mult)
-    v = _normal_bf16(rng, (B, Sk, Hkv, D))
-    dout = (torch.ones((B, Sq, H, D), dtype=torch.bfloat16) if dout_ones
-            else _normal_bf16(rng, (B, Sq, H, D)))
+    q = _normal(rng, (B, Sq, H, D), dtype=dtype)
+    k = _normal(rng, (B, Sk, Hkv, D), k_mult, dtype=dtype)
+    v = _normal(rng, (B, Sk, Hkv, D), dtype=dtype)
+    dout = (torch.ones((B, Sq, H, D), dtype=dtype) if dout_ones
+            else _normal(rng, (B, Sq, H, D), dtype=dtype))
     return Problem(name, q, k, v, dout, causal=causal,
-                   meta=dict(B=B, Sq=Sq, Sk=Sk, H=H, Hkv=Hkv, D=D, seed=seed, k_mult=k_mult))
+                   meta=dict(B=B, Sq=Sq, Sk=Sk, H=H, Hkv=Hkv, D=D, seed=seed, k_mult=k_mult,
+                             dtype=str(dtype)))
 
 
 def dv_nan_repro(seed=42):
@@ -98,7 +101,8 @@ def dv_nan_repro(seed=42):
     return p
 
 
-def padded_tile(sq, sk, mask_kind="bool", seed=2000, D=128, B=2, H=4, anti_row=True):
+def padded_tile(sq, sk, mask_kind="bool", seed=2000, D=128, B=2, H=4, anti_row=True,
+                dtype=torch.bfloat16):
     """Shapes off the 128-key tile, with one anti-aligned low-LSE query row per (b, h).
 
     Mask ([B, 1, sq, sk]): keep_bij = (j < L_b) and (u_bij >= 0.1 or j == 0) with
@@ -106,8 +110,8 @@ def padded_tile(sq, sk, mask_kind="bool", seed=2000, D=128, B=2, H=4, anti_row=T
     in bf16. "keypad" is a key-broadcast [B, 1, 1, sk] bool mask keep_bj = j < L_b.
     Anti-aligned row, per (b, h): a random unit vector u and a unit w orthogonal to it;
     every key of the head becomes n_j - (n_j . u) u + 16 u and the query row becomes
-    -84 u + 8 w, all rounded to bf16. The row is sq - 1 (inside the last, partial query
-    tile) for b = 0 and sq // 2 for b = 1.
+    -84 u + 8 w, all rounded to `dtype` (bf16 or fp16). The row is sq - 1 (inside the last,
+    partial query tile) for b = 0 and sq // 2 for b = 1. The additive mask is bf16 either way.
     """
     rng = _rng(seed)
     q32 = rng.standard_normal(size=(B, sq, H, D), dtype=np.float32)
@@ -128,7 +132,7 @@ def padded_tile(sq, sk, mask_kind="bool", seed=2000, D=128, B=2, H=4, anti_row=T
                 n = k32[b, :, h].astype(np.float64)
                 k32[b, :, h] = (n - np.outer(n @ u, u) + 16.0 * u).astype(np.float32)
                 q32[b, r, h] = (-84.0 * u + 8.0 * w).astype(np.float32)
-    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16)  # noqa: E731
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dtype)  # noqa: E731
     mask = None
     L = [sk, int(math.ceil(0.75 * sk))][:B] + [sk] * max(0, B - 2)
     if mask_kind in ("bool", "additive"):
@@ -154,16 +158,17 @@ def padded_tile(sq, sk, mask_kind="bool", seed=2000, D=128, B=2, H=4, anti_row=T
                    meta=dict(B=B, Sq=sq, Sk=sk, H=H, Hkv=H, D=D, seed=seed, anti_rows=rows))
 
 
-def wide_logit(s, seed=None, B=2, S=8192, H=32, D=128):
+def wide_logit(s, seed=None, B=2, S=8192, H=32, D=128, dtype=torch.bfloat16):
     """B2 S8192 H32 D128 non-causal, k = bf16(N(0,1) * s), dout ~ N(0,1)."""
     seed = 3000 + int(s) if seed is None else seed
-    p = dense(B, S, S, H, H, D, seed, causal=False, k_mult=float(s), name=f"wide_logit_s{s}")
+    p = dense(B, S, S, H, H, D, seed, causal=False, k_mult=float(s), name=f"wide_logit_s{s}",
+              dtype=dtype)
     p.meta["k_scale"] = s
     return p
 
 
 def varlen_gqa(seed=4000, nseq=16, lmin=128, lmax=4096, H=32, Hkv=8, D=128, extra_rows=0,
-               lengths=None, causal=True):
+               lengths=None, causal=True, dtype=torch.bfloat16):
     """Packed THD sequences, total_q = total_k, GQA, causal by default.
 
     ``extra_rows`` appends rows past cu_seqlens[-1] (their outputs must still be written).
@@ -175,10 +180,10 @@ def varlen_gqa(seed=4000, nseq=16, lmin=128, lmax=4096, H=32, Hkv=8, D=128, extr
     lengths = np.asarray(lengths, dtype=np.int64)
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     T = int(cu[-1]) + int(extra_rows)
-    q = _normal_bf16(rng, (T, H, D))
-    k = _normal_bf16(rng, (T, Hkv, D))
-    v = _normal_bf16(rng, (T, Hkv, D))
-    dout = _normal_bf16(rng, (T, H, D))
+    q = _normal(rng, (T, H, D), dtype=dtype)
+    k = _normal(rng, (T, Hkv, D), dtype=dtype)
+    v = _normal(rng, (T, Hkv, D), dtype=dtype)
+    dout = _normal(rng, (T, H, D), dtype=dtype)
     cu_t = torch.from_numpy(cu.copy())
     return Problem(f"varlen_gqa_n{len(lengths)}", q, k, v, dout, causal=causal,
                    cu_seqlens_q=cu_t, cu_seqlens_k=cu_t.clone(),

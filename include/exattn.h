@@ -39,7 +39,7 @@
  * non-OK status nothing was enqueued and no output was touched, except EXATTN_ERR_HIP,
  * which reports a failed kernel launch. exattn_last_error() gives a per-thread message.
  * Rejected instead of run (cudnn-frontend PR #429, second and third commit messages;
- * cudnn-frontend PR #9, item 4): a dtype other than bf16, a head_dim other than 64 or 128,
+ * cudnn-frontend PR #9, item 4): a dtype other than bf16 or fp16, a head_dim other than 64 or 128,
  * heads_q not a multiple of heads_kv, unaligned pointers or strides, a mask together with
  * cu_seqlens, a non-finite scale.
  */
@@ -58,7 +58,7 @@ extern "C" {
 typedef enum exattn_status {
   EXATTN_OK = 0,
   EXATTN_ERR_NULL = 1,       /* a required pointer is NULL */
-  EXATTN_ERR_DTYPE = 2,      /* dtype is not EXATTN_DTYPE_BF16 */
+  EXATTN_ERR_DTYPE = 2,      /* dtype is neither EXATTN_DTYPE_BF16 nor EXATTN_DTYPE_FP16 */
   EXATTN_ERR_HEAD_DIM = 3,   /* head_dim not in {64, 128} */
   EXATTN_ERR_SHAPE = 4,      /* negative sizes, heads_q % heads_kv != 0, size overflow */
   EXATTN_ERR_STRIDE = 5,     /* a stride is negative or not a multiple of 8 elements */
@@ -70,6 +70,10 @@ typedef enum exattn_status {
   EXATTN_ERR_HIP = 11        /* a HIP launch failed; see exattn_last_error() */
 } exattn_status;
 
+/* Element type of q, k, v, out, dout, dq, dk, dv (all the same). fp16 is threaded through
+ * every kernel instead of being rejected (cudnn-frontend PR #429, the fp16 follow-up
+ * commit: the element type reaches the kernel rather than being hard-coded). Additive
+ * masks are bf16 for either type. */
 typedef enum exattn_dtype { EXATTN_DTYPE_BF16 = 0, EXATTN_DTYPE_FP16 = 1 } exattn_dtype;
 
 typedef enum exattn_mask_kind {
@@ -100,7 +104,7 @@ typedef enum exattn_mask_kind {
  * of 0 broadcasts that axis (key-broadcast and per-batch masks); mask_stride[3] must be 1.
  */
 typedef struct exattn_problem {
-  int32_t dtype;         /* exattn_dtype; only EXATTN_DTYPE_BF16 is accepted */
+  int32_t dtype;         /* exattn_dtype */
   int32_t batch;         /* dense: batch size; packed: ignored */
   int32_t seqlen_q;      /* dense: query length; packed: total query rows */
   int32_t seqlen_k;      /* dense: key length; packed: total key rows */
@@ -134,10 +138,10 @@ int exattn_abi_version(void);
 exattn_status exattn_check(const exattn_problem* p);
 
 /*
- * Forward. q, k, v: bf16 device pointers laid out as described above. out: bf16 device
- * pointer, written contiguous ([batch, seqlen_q, heads_q, head_dim] or packed
- * [seqlen_q, heads_q, head_dim]); its o_stride entry is ignored. lse: fp32 device pointer
- * (layout above). Every element of out and lse is written.
+ * Forward. q, k, v: device pointers of the problem's dtype laid out as described above.
+ * out: device pointer of that dtype, written contiguous ([batch, seqlen_q, heads_q,
+ * head_dim] or packed [seqlen_q, heads_q, head_dim]); its o_stride entry is ignored.
+ * lse: fp32 device pointer (layout above). Every element of out and lse is written.
  */
 exattn_status exattn_fwd(const exattn_problem* p, const void* q, const void* k,
                          const void* v, void* out, float* lse, void* stream);
@@ -147,9 +151,11 @@ exattn_status exattn_fwd(const exattn_problem* p, const void* q, const void* k,
 size_t exattn_bwd_workspace_size(const exattn_problem* p);
 
 /*
- * Backward. q, k, v, out, dout: bf16 device inputs (strides in p); lse: fp32 device input
- * as written by exattn_fwd for the same problem (read only). dq, dk, dv: bf16 device
- * outputs, contiguous, every element written. workspace: device memory of at least
+ * Backward. q, k, v, out, dout: device inputs of the problem's dtype (strides in p); lse:
+ * fp32 device input as written by exattn_fwd for the same problem (read only). dq, dk, dv:
+ * device outputs of that dtype, contiguous, every element written. The fused variant (see
+ * exattn_set_variant) applies to bf16 only; fp16 problems always take the default split
+ * backward. workspace: device memory of at least
  * exattn_bwd_workspace_size(p) bytes, 256-byte aligned, owned by the caller; its contents
  * on entry do not matter and on exit are unspecified. Concurrent calls must not share a
  * workspace. With the default backward variant every output (dq included) is bitwise

@@ -88,6 +88,7 @@ def _problem(**kw):
 
 def test_check_accepts_valid_problem(lib):
     assert lib.exattn_check(ctypes.byref(_problem())) == 0
+    assert lib.exattn_check(ctypes.byref(_problem(dtype=1))) == 0   # fp16
     assert lib.exattn_check(ctypes.byref(_problem(head_dim=64, q_stride=(100 * 256, 256, 64),
                                                   k_stride=(77 * 128, 128, 64),
                                                   v_stride=(77 * 128, 128, 64)))) == 0
@@ -95,7 +96,8 @@ def test_check_accepts_valid_problem(lib):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dtype=1), 2),                        # fp16 is rejected, not run as bf16
+    (dict(dtype=2), 2),                        # an unknown dtype is rejected, not run as bf16
+    (dict(dtype=-1), 2),
     (dict(head_dim=96), 3),                    # only 64 and 128
     (dict(head_dim=256), 3),
     (dict(heads_q=6, heads_kv=4), 4),          # not a multiple

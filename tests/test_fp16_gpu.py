@@ -1,0 +1,61 @@
+"""fp16 inputs through every kernel (cudnn-frontend PR #429: the fp16 follow-up threads the
+input dtype into the kernel instead of hard-coding bf16 and checks fp16 numerically
+against a higher-precision reference; the failure it fixed was fp16 data run as bf16,
+with ~96% of dq elements outside tolerance).
+
+Besides the common bars, fp16 results must be at least several times closer to the
+float64 oracle than bf16 ones (fp16 keeps 3 more mantissa bits): a kernel that rounds
+anything through bf16 on the fp16 path fails FP16_TOL."""
+
+import pytest
+import torch
+
+from exact_attention_40_amd import api, workloads
+from gpu_util import compare, nonfinite, run_gpu, run_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+F16 = torch.float16
+FP16_TOL = dict(out=1.2e-3, lse=1.2e-3, dq=1.5e-3, dk=1.5e-3, dv=1.5e-3)
+
+CASES = [
+    dict(name="dense_d128", make=lambda: workloads.dense(2, 700, 650, 4, 2, 128, seed=8001, dtype=F16)),
+    dict(name="causal_d128", make=lambda: workloads.dense(1, 900, 900, 4, 4, 128, seed=8002,
+                                                          causal=True, dtype=F16)),
+    dict(name="causal_d64", make=lambda: workloads.dense(1, 333, 333, 2, 1, 64, seed=8003,
+                                                         causal=True, dtype=F16)),
+    dict(name="bool_mask", make=lambda: workloads.padded_tile(360, 64, mask_kind="bool", seed=8004,
+                                                              dtype=F16)),
+    dict(name="additive_mask", make=lambda: workloads.padded_tile(100, 77, mask_kind="additive",
+                                                                  seed=8005, dtype=F16)),
+    dict(name="varlen_gqa", make=lambda: workloads.varlen_gqa(seed=8006, nseq=3, lmin=100,
+                                                              lmax=700, H=4, Hkv=2, dtype=F16)),
+    dict(name="wide_logit_k8", make=lambda: workloads.wide_logit(8, B=1, S=1200, H=2, D=128,
+                                                                 dtype=F16)),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_fp16_parity(case):
+    p = case["make"]()
+    g = run_gpu(p)
+    for n in ("out", "dq", "dk", "dv"):
+        assert g[n].dtype == F16, n
+        assert nonfinite(g[n]) == 0, n
+    rep = compare(g, run_oracle(p), tag=f"fp16 {case['name']}")
+    for n, e in rep.items():
+        assert e <= FP16_TOL[n], f"fp16 {case['name']} {n}: rel-L2 {e:.3e} > {FP16_TOL[n]:.1e}"
+
+
+def test_fp16_ignores_fused_variant():
+    """Backward variant 1 (bf16 atomics) leaves fp16 on the split path: same bits."""
+    p = CASES[0]["make"]()
+    base = run_gpu(p)
+    try:
+        api.set_variant(1, 1)
+        other = run_gpu(p)
+    finally:
+        api.set_variant(1, 0)
+    for n in ("out", "lse", "dq", "dk", "dv"):
+        assert torch.equal(base[n], other[n]), n
+    say("fp16 fused-variant fallback ok")

@@ -127,10 +127,17 @@ def _qkv(B=1, S=64, H=2, D=128, dtype=torch.bfloat16, device="cuda"):
     return mk(), mk(), mk()
 
 
-def test_rejects_fp16_and_bad_head_dim():
+def test_rejects_other_dtypes_and_bad_head_dim():
+    """Unsupported inputs are rejected instead of run with the wrong element type
+    (cudnn-frontend PR #429, second commit message: an fp16 tensor run as bf16 returns
+    silently wrong gradients)."""
+    for dt in (torch.float32, torch.float64):
+        q, k, v = _qkv(dtype=dt)
+        with pytest.raises(ValueError, match="bfloat16 or torch.float16"):
+            api.exattn_fwd(q, k, v)
     q, k, v = _qkv(dtype=torch.float16)
-    with pytest.raises(ValueError, match="bfloat16"):
-        api.exattn_fwd(q, k, v)
+    with pytest.raises(ValueError, match="dtype"):
+        api.exattn_fwd(q, k.bfloat16(), v)                          # mixed input dtypes
     for D in (96, 100, 112, 192, 256):
         q, k, v = _qkv(D=D)
         with pytest.raises(ValueError, match="head_dim"):
