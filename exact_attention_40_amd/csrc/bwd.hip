@@ -209,10 +209,11 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
   // ---- per-lane LDS base addresses; everything else is an immediate offset ----------------
   // Row-operand reads of Q/dO rows qb*32 + l32, d-slab ds: one base per slab (the swizzle
   // depends on the row's low four bits only, so qb, the buffer and Q/dO are immediates).
-  const unsigned char* aq[T::DS];   // Q buffer 0 (+QBYTES for buffer 1, +DO_OFF for dO)
+  // Wave A reads Q (S = Q K^T), wave B reads dO (dP = dO V^T).
+  const unsigned char* aq[T::DS];   // buffer 0; +QBYTES for buffer 1
 #pragma unroll
   for (int ds = 0; ds < T::DS; ++ds)
-    aq[ds] = q_b + l32 * RB + 16 * ((2 * ds + half) ^ swz_f<D>(l32));
+    aq[ds] = q_b + (role_a ? 0 : DO_OFF) + l32 * RB + 16 * ((2 * ds + half) ^ swz_f<D>(l32));
   // Transposed reads of dO (wave A) or Q (wave B): rows 16kk + 4*half + (j16>>2) + 8*sec,
   // columns db*32 + 16*(grp&1) + 4*(j16&3); one base per (db, sec), kk is an immediate.
   const int tr_row = j16 >> 2;
@@ -359,16 +360,21 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
     };
 
     // ---- phase 1: S and P (A) / dP (B) ----
+    // Row fragments are read four MFMAs ahead; the fences keep the reads where they are
+    // placed so the LDS latency overlaps the preceding MFMAs.
     f32x16 sp[T::QB];
 #pragma unroll
     for (int qb = 0; qb < T::QB; ++qb) sp[qb] = f32x16{};
     {
-      const int po = role_a ? 0 : DO_OFF;    // A multiplies Q by K, B multiplies dO by V
+      constexpr int NF = T::DS * T::QB;
+      auto frag = [&](int f) { return lds_at<V8>(aq[f / T::QB], QO + (f % T::QB) * 32 * RB); };
+      V8 fr[4] = {frag(0), frag(1), frag(2), frag(3)};
 #pragma unroll
-      for (int ds = 0; ds < T::DS; ++ds) {
-#pragma unroll
-        for (int qb = 0; qb < T::QB; ++qb)
-          sp[qb] = mfma32(lds_at<V8>(aq[ds] + po, QO + qb * 32 * RB), kv[ds], sp[qb]);
+      for (int f = 0; f < NF; ++f) {
+        const int ds = f / T::QB, qb = f % T::QB;
+        sp[qb] = mfma32(fr[f % 4], kv[ds], sp[qb]);
+        if (f + 4 < NF) fr[f % 4] = frag(f + 4);
+        __builtin_amdgcn_sched_barrier(0x0004);
       }
     }
     if (role_a) {
@@ -404,16 +410,29 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
         }
       }
     }
+    // Transposed fragments of the next 16-row slab are read while this slab's MFMAs run.
+    {
+      constexpr int NKK = T::BM / 16;
+      V4 tb[2][T::DB][2];
+      auto tload = [&](int kk, int slot) {
 #pragma unroll
-    for (int kk = 0; kk < T::BM / 16; ++kk) {
-      const int qb = kk >> 1, hs = (kk & 1) * 8;
-      const V8 pa = cvt8<V8>(sp[qb][hs + 0], sp[qb][hs + 1], sp[qb][hs + 2], sp[qb][hs + 3],
-                             sp[qb][hs + 4], sp[qb][hs + 5], sp[qb][hs + 6], sp[qb][hs + 7]);
+        for (int db = 0; db < T::DB; ++db) {
+          tb[slot][db][0] = tr_at<V4>(tq[db][0], QO + 16 * kk * RB);
+          tb[slot][db][1] = tr_at<V4>(tq[db][1], QO + 16 * kk * RB);
+        }
+      };
+      tload(0, 0);
 #pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-        const int o = QO + 16 * kk * RB;
-        const V8 bv = cat44(tr_at<V4>(tq[db][0], o), tr_at<V4>(tq[db][1], o));
-        acc[db] = mfma32(pa, bv, acc[db]);
+      for (int kk = 0; kk < NKK; ++kk) {
+        const int qb = kk >> 1, hs = (kk & 1) * 8;
+        const V8 pa = cvt8<V8>(sp[qb][hs + 0], sp[qb][hs + 1], sp[qb][hs + 2], sp[qb][hs + 3],
+                               sp[qb][hs + 4], sp[qb][hs + 5], sp[qb][hs + 6], sp[qb][hs + 7]);
+        if (kk + 1 < NKK) tload(kk + 1, (kk + 1) & 1);
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) {
+          acc[db] = mfma32(pa, cat44(tb[kk & 1][db][0], tb[kk & 1][db][1]), acc[db]);
+          __builtin_amdgcn_sched_barrier(0x0004);
+        }
       }
     }
     // Tile it + 1 was requested during the previous dQ phase; only the newest memory
@@ -620,15 +639,24 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr int KO = BUF * T::TBYTES;
     if (t + 1 < ntiles) load_tile(t + 1, BUF ^ 1);
+    // S^T and dP^T: K and V row fragments read four MFMAs ahead (fences keep the order).
     f32x16 s[T::KB], dp[T::KB];
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb) s[kb] = dp[kb] = f32x16{};
+    {
+      constexpr int NF = T::DS * T::KB * 2;    // (ds, kb, K or V)
+      auto frag = [&](int f) {
+        const int ds = f / (2 * T::KB), kb = (f / 2) % T::KB, isv = f & 1;
+        return lds_at<V8>(ar[ds], isv * V_OFF + KO + kb * 32 * RB);
+      };
+      V8 fr[4] = {frag(0), frag(1), frag(2), frag(3)};
 #pragma unroll
-    for (int ds = 0; ds < T::DS; ++ds) {
-#pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) {
-        s[kb] = mfma32(lds_at<V8>(ar[ds], KO + kb * 32 * RB), qf[ds], s[kb]);
-        dp[kb] = mfma32(lds_at<V8>(ar[ds], V_OFF + KO + kb * 32 * RB), df[ds], dp[kb]);
+      for (int f = 0; f < NF; ++f) {
+        const int ds = f / (2 * T::KB), kb = (f / 2) % T::KB;
+        if (f & 1) dp[kb] = mfma32(fr[f % 4], df[ds], dp[kb]);
+        else s[kb] = mfma32(fr[f % 4], qf[ds], s[kb]);
+        if (f + 4 < NF) fr[f % 4] = frag(f + 4);
+        __builtin_amdgcn_sched_barrier(0x0004);
       }
     }
     const int kb0 = t * T::BN;
@@ -660,17 +688,30 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
         dp[kb][r] = p * (dp[kb][r] - dl);
       }
     }
-    // dQ^T += K^T dS^T over 16-key slabs.
+    // dQ^T += K^T dS^T over 16-key slabs; the next slab's transposed K fragments are read
+    // while this slab's MFMAs run.
+    {
+      constexpr int NKK = T::BN / 16;
+      V4 tb[2][T::DB][2];
+      auto tload = [&](int kk, int slot) {
 #pragma unroll
-    for (int kk = 0; kk < T::BN / 16; ++kk) {
-      const int kb = kk >> 1, hs = (kk & 1) * 8;
-      const V8 sb = cvt8<V8>(dp[kb][hs + 0], dp[kb][hs + 1], dp[kb][hs + 2], dp[kb][hs + 3],
-                             dp[kb][hs + 4], dp[kb][hs + 5], dp[kb][hs + 6], dp[kb][hs + 7]);
+        for (int db = 0; db < T::DB; ++db) {
+          tb[slot][db][0] = tr_at<V4>(tk[db][0], KO + 16 * kk * RB);
+          tb[slot][db][1] = tr_at<V4>(tk[db][1], KO + 16 * kk * RB);
+        }
+      };
+      tload(0, 0);
 #pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-        const int o = KO + 16 * kk * RB;
-        const V8 ka = cat44(tr_at<V4>(tk[db][0], o), tr_at<V4>(tk[db][1], o));
-        dq[db] = mfma32(ka, sb, dq[db]);
+      for (int kk = 0; kk < NKK; ++kk) {
+        const int kb = kk >> 1, hs = (kk & 1) * 8;
+        const V8 sb = cvt8<V8>(dp[kb][hs + 0], dp[kb][hs + 1], dp[kb][hs + 2], dp[kb][hs + 3],
+                               dp[kb][hs + 4], dp[kb][hs + 5], dp[kb][hs + 6], dp[kb][hs + 7]);
+        if (kk + 1 < NKK) tload(kk + 1, (kk + 1) & 1);
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) {
+          dq[db] = mfma32(cat44(tb[kk & 1][db][0], tb[kk & 1][db][1]), sb, dq[db]);
+          __builtin_amdgcn_sched_barrier(0x0004);
+        }
       }
     }
     wait_vmem();      // the next tile has landed in LDS
