@@ -153,6 +153,9 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
   const bool role_a = wave < T::KG;
   const int kg = role_a ? wave : wave - T::KG;   // key group of this wave
 
+  // Consecutive blocks are the key blocks of one (unit, kv head): they re-read the same
+  // Q/dO tiles, which then stay in one XCD's L2 (also for packed layouts, where ordering
+  // by key block across sequences was measured slower).
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int kbi = blk % a.num_k_blocks;
   const int ug = blk / a.num_k_blocks;
@@ -532,12 +535,20 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31, grp = lane >> 4, j16 = lane & 15;
 
+  // Block order as in the forward: packed layouts take the query-tile index outermost.
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int n_qtiles = a.num_q_blocks;
-  int qtile = blk % n_qtiles;
-  const int uh = blk / n_qtiles;
+  int qtile, uh;
+  if constexpr (VARLEN) {
+    const int nuh = a.num_units * a.H;
+    qtile = n_qtiles - 1 - blk / nuh;
+    uh = blk % nuh;
+  } else {
+    qtile = blk % n_qtiles;
+    uh = blk / n_qtiles;
+    if (CAUSAL) qtile = n_qtiles - 1 - qtile;    // longest rows first
+  }
   const int head = uh % a.H, unit = uh / a.H, g = head / a.group;
-  if (CAUSAL) qtile = n_qtiles - 1 - qtile;      // longest rows first
 
   int Sq, Sk;
   int64_t qrow0, q_base, k_base, v_base, do_base, st_base, m_base = 0;

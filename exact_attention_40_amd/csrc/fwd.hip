@@ -75,11 +75,21 @@ fwd_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform across the wave
   const int half = lane >> 5, l32 = lane & 31;
 
+  // Dense: consecutive blocks are the query tiles of one (unit, head), which share K/V in
+  // one XCD's L2. Packed: query-tile index outermost, highest first, so that the longest
+  // blocks of every sequence (whatever its length) start before the short ones.
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  int qtile = blk % a.num_q_tiles;
-  const int uh = blk / a.num_q_tiles;
+  int qtile, uh;
+  if constexpr (VARLEN) {
+    const int nuh = a.num_units * a.H;
+    qtile = a.num_q_tiles - 1 - blk / nuh;
+    uh = blk % nuh;
+  } else {
+    qtile = blk % a.num_q_tiles;
+    uh = blk / a.num_q_tiles;
+    if (CAUSAL) qtile = a.num_q_tiles - 1 - qtile;  // longest rows first
+  }
   const int head = uh % a.H, unit = uh / a.H, g = head / a.group;
-  if (CAUSAL) qtile = a.num_q_tiles - 1 - qtile;  // longest rows first
 
   int Sq, Sk;
   int64_t q_base, k_base, v_base, o_base, lse_base, m_base = 0;
