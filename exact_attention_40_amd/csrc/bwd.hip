@@ -536,17 +536,23 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
   const int half = lane >> 5, l32 = lane & 31, grp = lane >> 4, j16 = lane & 15;
 
   // Block order as in the forward: packed layouts take the query-tile index outermost.
+  // Dense causal: tiles n-1-j and j in one workgroup (equal work per block).
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
   const int n_qtiles = a.num_q_blocks;
-  int qtile, uh;
+  int qtile, qtile2 = -1, uh;
   if constexpr (VARLEN) {
     const int nuh = a.num_units * a.H;
     qtile = n_qtiles - 1 - blk / nuh;
     uh = blk % nuh;
+  } else if constexpr (CAUSAL) {
+    const int npair = (n_qtiles + 1) / 2;
+    const int j = blk % npair;
+    uh = blk / npair;
+    qtile = n_qtiles - 1 - j;
+    if (j != qtile) qtile2 = j;
   } else {
     qtile = blk % n_qtiles;
     uh = blk / n_qtiles;
-    if (CAUSAL) qtile = n_qtiles - 1 - qtile;    // longest rows first
   }
   const int head = uh % a.H, unit = uh / a.H, g = head / a.group;
 
@@ -573,6 +579,8 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
     st_base = ((int64_t)unit * a.H + head) * a.Sq;
     m_base = (int64_t)unit * a.m_sb + (int64_t)head * a.m_sh;
   }
+  // One query tile of BM rows; the workgroup runs one or two of them.
+  auto run_tile = [&](const int qtile) __attribute__((always_inline)) {
   const int qt0 = qtile * T::BM;
   if (qt0 >= Sq) return;
   const E* K = reinterpret_cast<const E*>(a.k) + k_base;
@@ -751,6 +759,13 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
   E* dqw = reinterpret_cast<E*>(a.dq) + ((qrow0 + qw0) * a.H + head) * D;
   static_assert(T::NW * 32 * D * 2 <= 4 * T::TBYTES, "epilogue staging fits the tile buffers");
   wave_store_rows<D, E>(smem + wave * 32 * D * 2, dq, a.scale, dqw, (int64_t)a.H * D, Sq - qw0, lane);
+  };
+
+  run_tile(qtile);
+  if (qtile2 >= 0) {
+    __syncthreads();  // the first tile's epilogue is done with LDS
+    run_tile(qtile2);
+  }
 }
 
 // ----------------------------------------------------------------------------------------
@@ -885,7 +900,8 @@ hipError_t launch_bwd(const BwdArgs& a, int head_dim, int dtype, bool causal, in
 template <class E, int D>
 static hipError_t launch_bwd_dq_d(const BwdArgs& a, bool causal, int mask, bool varlen,
                                   hipStream_t s) {
-  const int64_t nblk = (int64_t)a.num_units * a.H * a.num_q_blocks;
+  const int per = (causal && !varlen) ? (a.num_q_blocks + 1) / 2 : a.num_q_blocks;
+  const int64_t nblk = (int64_t)a.num_units * a.H * per;
   if (nblk <= 0) return hipSuccess;
   dim3 grid((unsigned)nblk), block(512);
 #define EXATTN_DQ(C, M, V) hipLaunchKernelGGL((bwd_dq_kernel<E, D, C, M, V>), grid, block, 0, s, a)

@@ -78,16 +78,24 @@ fwd_kernel(FwdArgs a) {
   // Dense: consecutive blocks are the query tiles of one (unit, head), which share K/V in
   // one XCD's L2. Packed: query-tile index outermost, highest first, so that the longest
   // blocks of every sequence (whatever its length) start before the short ones.
+  // Dense causal: block j of a (unit, head) runs query tiles n-1-j and j one after the
+  // other (tile i sees i+1 key tiles), so every block has the same amount of work and no
+  // long tile is left for the end of the grid.
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  int qtile, uh;
+  int qtile, qtile2 = -1, uh;
   if constexpr (VARLEN) {
     const int nuh = a.num_units * a.H;
     qtile = a.num_q_tiles - 1 - blk / nuh;
     uh = blk % nuh;
+  } else if constexpr (CAUSAL) {
+    const int npair = (a.num_q_tiles + 1) / 2;
+    const int j = blk % npair;
+    uh = blk / npair;
+    qtile = a.num_q_tiles - 1 - j;
+    if (j != qtile) qtile2 = j;
   } else {
     qtile = blk % a.num_q_tiles;
     uh = blk / a.num_q_tiles;
-    if (CAUSAL) qtile = a.num_q_tiles - 1 - qtile;  // longest rows first
   }
   const int head = uh % a.H, unit = uh / a.H, g = head / a.group;
 
@@ -112,6 +120,8 @@ fwd_kernel(FwdArgs a) {
     lse_base = ((int64_t)unit * a.H + head) * a.Sq;
     m_base = (int64_t)unit * a.m_sb + (int64_t)head * a.m_sh;
   }
+  // One query tile of BM rows; the workgroup runs one or two of them.
+  auto run_tile = [&](const int qtile) __attribute__((always_inline)) {
   const int qt0 = qtile * T::BM;
   if (qt0 >= Sq) return;
 
@@ -474,6 +484,13 @@ fwd_kernel(FwdArgs a) {
       a.lse[lse_base + qi[qb]] = l > 0.f ? (mu + log2f(l)) * kLn2 : -INFINITY;
     }
   }
+  };
+
+  run_tile(qtile);
+  if (qtile2 >= 0) {
+    __syncthreads();  // the first tile's epilogue is done with LDS
+    run_tile(qtile2);
+  }
 }
 
 // Rows of a packed output past cu_seqlens_q[num_seqs]: out = 0, lse = -inf.
@@ -505,9 +522,15 @@ static int effective_variant(int head_dim, int dtype, int mask, bool varlen) {
 
 int fwd_block_m(int head_dim, int mask, bool varlen) { return 256; }
 
+// Blocks per (unit, head): one per query tile, or one per pair of tiles (dense causal).
+static int64_t fwd_blocks(const FwdArgs& a, bool causal, bool varlen) {
+  const int per = (causal && !varlen) ? (a.num_q_tiles + 1) / 2 : a.num_q_tiles;
+  return (int64_t)a.num_units * a.H * per;
+}
+
 template <class E, int D, int NW, int QB, bool LAZY>
 static hipError_t launch_fwd_d(const FwdArgs& a, bool causal, int mask, bool varlen, hipStream_t s) {
-  const int64_t nblk = (int64_t)a.num_units * a.H * a.num_q_tiles;
+  const int64_t nblk = fwd_blocks(a, causal, varlen);
   if (nblk <= 0) return hipSuccess;
   dim3 grid((unsigned)nblk), block(64 * NW);
 #define EXATTN_FWD(C, M, V) \
@@ -530,7 +553,7 @@ static hipError_t launch_fwd_d(const FwdArgs& a, bool causal, int mask, bool var
 
 template <int NW, int QB>
 static hipError_t launch_fwd_plain128(const FwdArgs& a, bool causal, hipStream_t s) {
-  const int64_t nblk = (int64_t)a.num_units * a.H * a.num_q_tiles;
+  const int64_t nblk = fwd_blocks(a, causal, false);
   if (nblk <= 0) return hipSuccess;
   dim3 grid((unsigned)nblk), block(64 * NW);
   if (causal)
