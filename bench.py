@@ -73,7 +73,7 @@ def cpu_baseline(target_seconds=15.0):
     flops = 0.0
     units = 0
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < target_seconds and units < 8:
+    while time.perf_counter() - t0 < target_seconds and units < 16:
         p = workloads.dense(1, S, S, 1, 1, D, seed=int(rng.integers(1 << 30)))
         q, k, v, do = (t.double().numpy() for t in (p.q, p.k, p.v, p.dout))
         oracle.attention_forward(q, k, v)

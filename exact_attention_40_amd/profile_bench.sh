@@ -1,7 +1,7 @@
 #!/bin/bash
 # rocprofv3 passes over bench.py (kernel trace + stats, then FETCH_SIZE and WRITE_SIZE) and
 # over copy_probe (the same two counters) for the HBM-traffic calibration. Writes raw output
-# under gpurun_out/prof and the per-kernel traffic JSON into profiles/.
+# and the per-kernel traffic JSON under gpurun_out/prof.
 set -o pipefail
 export TMPDIR=/tmp
 R=${GRAFT_REPO_ROOT:-$(cd "$(dirname "$0")/.." && pwd)}

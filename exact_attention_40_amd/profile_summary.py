@@ -1,0 +1,82 @@
+"""Writes the kernel-duration and HBM-traffic summary for profiles/ from the output of
+profile_bench.sh (rocprofv3 kernel stats CSV and the per-kernel traffic JSON files).
+
+    python -m exact_attention_40_amd.profile_summary PROF_DIR OUT.md
+"""
+
+import csv
+import json
+import os
+import re
+import sys
+
+from .traffic import KERNELS, matches
+
+MIN_BYTES = {  # algorithmic bytes per launch at B=2 S=8192 H=32 D=128 (bf16 tensors 134.2 MB, row vectors 2.1 MB)
+    "exattn_fwd_kernel": ("q, k, v read 0.403 GB; out + lse written 0.136 GB", 0.4027, 0.1363),
+    "exattn_bwd_dkdv_kernel": ("q, k, v, dout 0.537 GB + lse2, delta 0.004 GB read; dk, dv 0.268 GB written", 0.5411, 0.2684),
+    "exattn_bwd_dq_kernel": ("q, k, v, dout 0.537 GB + stats 0.004 GB read; dq 0.134 GB written", 0.5411, 0.1342),
+    "exattn_bwd_delta_kernel": ("out, dout 0.268 GB + lse read; delta, lse2 0.004 GB written", 0.2705, 0.0042),
+}
+
+
+def short(name):
+    for k, t in KERNELS.items():
+        if matches(name, t):
+            return k
+    return name
+
+
+def main():
+    prof, out = sys.argv[1:3]
+    rows = list(csv.DictReader(open(os.path.join(prof, "trace", "bench_kernel_stats.csv"))))
+    lines = [
+        "# Kernel durations and HBM traffic: fwd + bwd step, B=2 S=8192 H=32 Hkv=32 D=128 (non-causal, bf16)",
+        "",
+        "Kernel trace (rocprofv3 `--kernel-trace --stats`) over 2 warm-up and 5 timed bench steps, so the",
+        "average includes the first (cold) calls; the minimum is the steady state that bench.py's",
+        "in-process HIP-event timing sees.",
+        "",
+        "Command (from the repository root; `exact_attention_40_amd/profile_bench.sh` runs all passes):",
+        "",
+        "```",
+        "rocprofv3 --kernel-trace --stats -d gpurun_out/prof/trace -o bench -f csv -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+        "```",
+        "",
+        "| kernel | instance | calls | avg ms | min ms | max ms | share |",
+        "|---|---|---|---|---|---|---|",
+    ]
+    for r in rows:
+        lines.append(f"| {short(r['Name'])} | `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
+                     f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} | {float(r['Percentage']):.1f}% |")
+    lines += [
+        "",
+        "HBM bytes per launch: `rocprofv3 --pmc FETCH_SIZE` and, in a second run, `--pmc WRITE_SIZE` over",
+        "`python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline`, each scaled by the same counter over",
+        "`python3 -m exact_attention_40_amd.copy_probe 512` (a copy of 512 MiB, three times).",
+    ]
+    recs = {}
+    for k in KERNELS:
+        p = os.path.join(prof, f"{k}_b2_s8192_h32_d128_pmc.json")
+        if os.path.exists(p):
+            recs[k] = json.load(open(p))
+    if recs:
+        cal = next(iter(recs.values()))["copy_calibration"]
+        lines += [
+            f"FETCH_SIZE reads 1/{cal['fetch_factor']:.3f} of the copied bytes, WRITE_SIZE 1/{cal['write_factor']:.3f}.",
+            "The per-kernel JSON files next to this one hold the numbers with the kernel source hash",
+            f"bench.py checks ({next(iter(recs.values()))['source_hash']}).",
+            "",
+            "| kernel | read GB | written GB | read / minimum | written / minimum | algorithmic minimum |",
+            "|---|---|---|---|---|---|",
+        ]
+        for k, r in recs.items():
+            desc, mr, mw = MIN_BYTES[k]
+            rd, wr = r["fetch_bytes_per_launch"] / 1e9, r["write_bytes_per_launch"] / 1e9
+            lines.append(f"| {k} | {rd:.3f} | {wr:.3f} | {rd / mr:.2f} | {wr / mw:.2f} | {desc} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -17,12 +17,19 @@ import json
 import os
 import sys
 
-KERNELS = {  # library timing name -> substring of the demangled kernel name
-    "exattn_fwd_kernel": "exattn::fwd_kernel<",
-    "exattn_bwd_dkdv_kernel": "exattn::bwd_kernel<",
-    "exattn_bwd_dq_kernel": "exattn::bwd_dq_kernel<",
-    "exattn_bwd_delta_kernel": "exattn::delta_kernel<",
+KERNELS = {  # library timing name -> kernel template name (rocprofv3 may or may not demangle)
+    "exattn_fwd_kernel": "fwd_kernel",
+    "exattn_bwd_dkdv_kernel": "bwd_kernel",
+    "exattn_bwd_dq_kernel": "bwd_dq_kernel",
+    "exattn_bwd_delta_kernel": "delta_kernel",
 }
+
+
+def matches(kernel_name, template):
+    """True when `kernel_name` (demangled or Itanium-mangled) is an instance of exattn::`template`."""
+    return (f"exattn::{template}<" in kernel_name
+            or f"N6exattn{len(template)}{template}I" in kernel_name
+            or f"ZN6exattn{len(template)}{template}I" in kernel_name)
 
 
 def source_hash():
@@ -59,8 +66,8 @@ def main():
     fetch, write = per_kernel(bf, "FETCH_SIZE"), per_kernel(bw, "WRITE_SIZE")
     shash = source_hash()
     for name, sub in KERNELS.items():
-        fk = [v for k, v in fetch.items() if sub in k]
-        wk = [v for k, v in write.items() if sub in k]
+        fk = [v for k, v in fetch.items() if matches(k, sub)]
+        wk = [v for k, v in write.items() if matches(k, sub)]
         if not fk or not wk:
             continue
         rec = {
