@@ -21,6 +21,11 @@ Workloads (the pages describe the shapes; every value here is synthetic):
 * ``varlen_gqa`` - 16 packed sequences with lengths uniform in [128, 4096], H32 Hkv8, causal.
 * ``long_causal`` - B1 S61380 H32 D128 causal (FlyDSL PR #1033, "Result": the shortest
   sequence length of its throughput table).
+* ``fp8_dense`` - fp8 e4m3 q, k, v with one descale per tensor for the fp8 forward
+  (FlyDSL PR #1033, "The fp8 helper, second commit": K scaled by a large factor, V = ones
+  in some of its runs). ``kind="normal"`` quantises N(0,1) draws (the descale maps the
+  largest magnitude to 448); ``kind="grid"`` draws q and k from {0, +-0.5, +-1, +-1.5, +-2}
+  and v from {+-0.5, +-1}, whose products and dot products are exact in fp32.
 """
 
 from __future__ import annotations
@@ -32,7 +37,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["Problem", "dense", "dv_nan_repro", "padded_tile", "wide_logit", "varlen_gqa",
+__all__ = ["Problem", "Fp8Problem", "fp8_dense", "dense", "dv_nan_repro", "padded_tile", "wide_logit", "varlen_gqa",
            "long_causal", "PADDED_TILE_SHAPES", "WIDE_LOGIT_SCALES"]
 
 PADDED_TILE_SHAPES = ((392, 392), (360, 64), (100, 77))
@@ -195,3 +200,50 @@ def long_causal(seed=5000, S=61380, H=32, D=128):
     """B1 S61380 H32 D128 causal, q, k, v, dout ~ N(0,1)."""
     p = dense(1, S, S, H, H, D, seed, causal=True, name="long_causal")
     return p
+
+
+@dataclass
+class Fp8Problem:
+    """fp8 e4m3 CPU tensors (torch.float8_e4m3fn) with their per-tensor descales."""
+    name: str
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    q_descale: float
+    k_descale: float
+    v_descale: float
+    causal: bool = False
+    scale: Optional[float] = None
+
+    def decoded(self):
+        """q, k, v as float64 NumPy arrays of their e4m3 values (descales not applied)."""
+        return tuple(t.to(torch.float64).numpy() for t in (self.q, self.k, self.v))
+
+
+def _quantise_e4m3(x):
+    """float32 array -> (e4m3 tensor, descale) with the largest magnitude mapped to 448."""
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    d = amax / 448.0 if amax > 0 else 1.0
+    return torch.from_numpy(x / np.float32(d)).to(torch.float8_e4m3fn), d
+
+
+def fp8_dense(B, Sq, Sk, H, Hkv, D, seed, *, causal=False, kind="normal", k_mult=1.0,
+              v_ones=False, name=None):
+    """Seeded fp8 inputs in BSHD layout. ``k_mult`` multiplies k's descale (the logit
+    spread); ``v_ones`` makes every value 1."""
+    rng = _rng(seed)
+    if kind == "grid":
+        qv = rng.integers(-4, 5, size=(B, Sq, H, D)).astype(np.float32) * 0.5
+        kv = rng.integers(-4, 5, size=(B, Sk, Hkv, D)).astype(np.float32) * 0.5
+        vv = rng.choice(np.array([-1.0, -0.5, 0.5, 1.0], dtype=np.float32), size=(B, Sk, Hkv, D))
+        q, k, v = (torch.from_numpy(t).to(torch.float8_e4m3fn) for t in (qv, kv, vv))
+        dq = dk = dvs = 1.0
+    else:
+        q, dq = _quantise_e4m3(rng.standard_normal(size=(B, Sq, H, D), dtype=np.float32))
+        k, dk = _quantise_e4m3(rng.standard_normal(size=(B, Sk, Hkv, D), dtype=np.float32))
+        v, dvs = _quantise_e4m3(rng.standard_normal(size=(B, Sk, Hkv, D), dtype=np.float32))
+    if v_ones:
+        v = torch.ones((B, Sk, Hkv, D), dtype=torch.float8_e4m3fn)
+        dvs = 1.0
+    return Fp8Problem(name or f"fp8_{kind}_b{B}_sq{Sq}_sk{Sk}_h{H}_{Hkv}_d{D}_k{k_mult:g}",
+                      q, k, v, dq, dk * k_mult, dvs, causal)

@@ -1,0 +1,140 @@
+"""Float64 CPU oracle for the fp8 forward with a bounded rebase of the running max.
+
+TEST INFRASTRUCTURE ONLY. The test suite, the package's smoke check and the benchmark's
+CPU-baseline leg may import this module; the product path never does, and nothing here
+is shared with the GPU library.
+
+Source: FlyDSL PR #1033, "[Bugfix][Kernel] Fix NaN from the lazy rescale on a wide score
+range", section "The fp8 helper, second commit". That section describes an fp8 forward
+whose softmax helper differs from the bf16 one in three ways, which this module follows
+step by step (it is an algorithm with quantised intermediates, not a closed form, so the
+oracle walks the key tiles in order):
+
+* the rescale test is applied to scores already multiplied by the logit scale, so the
+  threshold (8, log2 units) is measured on the scaled scores;
+* when the wave-wide test fires, a row does not keep max(m_row, m_tile): it is rebased
+  onto its own tile max even when that is lower than the running max, which keeps the
+  exponentials of the current tile near 1 where fp8 resolves them best;
+* the fix caps how far one rebase may lower the base at 16 (log2 units), so the factor
+  applied to the row's accumulators is at most 2**16. Without the cap a row dragged along
+  by another row's rise multiplies its sums by 2**(m_row - m_tile), which overflows on a
+  wide score range (the NaN the section reports).
+
+Readings where the section is silent (each is listed in the design notes):
+
+* inputs are OCP fp8 e4m3 (4 exponent bits, bias 7, 3 mantissa bits, largest finite 448)
+  with one float descale per tensor; the logit scale is scale * q_descale * k_descale
+  * log2(e), and v_descale multiplies the normalised output;
+* the exponentials p are rounded to e4m3 (nearest, ties to even) before the P.V product,
+  while the row sum l adds the unrounded p, as the bf16 path sums p before its bf16
+  rounding; hence lse is exact and only out carries the fp8 rounding of P;
+* the wave-wide test covers `group_rows` consecutive query rows (32 on the GPU: one row
+  per lane pair of a 64-wide wave), the key tile is `block_n` keys (64 on the GPU);
+* a row with no visible key so far keeps m = -inf, its factor is taken as 1 (its sums are
+  zero), and lse = (m + log2 l) * ln 2 is the natural-log LSE of the bf16 path.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = ["E4M3_MAX", "round_e4m3", "fp8_forward"]
+
+E4M3_MAX = 448.0
+_LOG2E = 1.0 / math.log(2.0)
+_LN2 = math.log(2.0)
+
+
+def round_e4m3(x):
+    """Nearest OCP e4m3 value of each element of x (ties to even), in float64.
+
+    Normal binades [2^e, 2^(e+1)) for e >= -6 hold 8 values spaced 2^(e-3); below 2^-6 the
+    subnormals are spaced 2^-9. Magnitudes above 448 are out of range and rejected (the
+    fp8 forward never produces them: every exponential is at most 2^8).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.any(a > E4M3_MAX):
+        raise ValueError("value beyond the e4m3 range")
+    _, e = np.frexp(a)                      # a = m * 2^e with 0.5 <= m < 1, so floor(log2 a) = e - 1
+    quantum = np.ldexp(1.0, np.maximum(e - 1, -6) - 3)
+    return np.copysign(np.round(a / quantum) * quantum, x)   # np.round: half to even
+
+
+def fp8_forward(q8, k8, v8, q_descale, k_descale, v_descale, *, causal=False, scale=None,
+                block_n=64, group_rows=32, tau=8.0, bound=16.0, quantize_p=True,
+                return_stats=False):
+    """fp8 attention forward, tile by tile as the FlyDSL fp8 helper does (see module doc).
+
+    q8 [B, Sq, H, D], k8 / v8 [B, Sk, Hkv, D]: float arrays holding e4m3 values (decoded,
+    without their descales). Returns out [B, Sq, H, D] and lse [B, H, Sq] in float64.
+    ``bound=None`` rebases without a cap (the behaviour before the fix);
+    ``quantize_p=False`` skips the e4m3 rounding of P (then the result is the exact
+    attention of the dequantised inputs, whatever the rebase sequence).
+    With ``return_stats`` a dict counts triggered tiles and rebases that lowered a base,
+    and those the cap limited.
+    """
+    q8, k8, v8 = (np.asarray(t, dtype=np.float64) for t in (q8, k8, v8))
+    B, Sq, H, D = q8.shape
+    Sk, Hkv = k8.shape[1], k8.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    c2 = scale * q_descale * k_descale * _LOG2E          # logit scale, log2 units
+    out = np.zeros((B, Sq, H, D))
+    lse = np.full((B, H, Sq), -np.inf)
+    stats = {"triggers": 0, "lowered": 0, "capped": 0}
+    group = np.arange(Sq) // group_rows
+    for b in range(B):
+        for h in range(H):
+            g = h // (H // Hkv)
+            s2 = (q8[b, :, h, :] @ k8[b, :, g, :].T) * c2          # [Sq, Sk]
+            m = np.full(Sq, -np.inf)
+            l = np.zeros(Sq)
+            acc = np.zeros((Sq, D))
+            for j0 in range(0, Sk, block_n):
+                cols = np.arange(j0, min(j0 + block_n, Sk))
+                vis = np.ones((Sq, cols.size), dtype=bool)
+                if causal:
+                    vis &= cols[None, :] <= np.arange(Sq)[:, None]
+                st = np.where(vis, s2[:, cols], -np.inf)
+                m_tile = st.max(axis=1)
+                # 1. rescale test per row (a row with m = -inf and a visible key fires:
+                #    +inf > tau), then made common to each group of rows
+                with np.errstate(invalid="ignore"):
+                    fire_row = (m_tile - m) > tau
+                fire_grp = np.zeros(group.max() + 1, dtype=bool)
+                np.logical_or.at(fire_grp, group, fire_row)
+                fire = fire_grp[group]
+                # 2. rebase: onto the row's tile max, lowering the base by at most `bound`
+                if fire.any():
+                    stats["triggers"] += int(fire_grp.sum())
+                    m_new = m_tile if bound is None else np.maximum(m_tile, m - bound)
+                    stats["lowered"] += int(np.sum(fire & (m_new < m)))
+                    if bound is not None:
+                        stats["capped"] += int(np.sum(fire & (m_tile < m - bound)))
+                    with np.errstate(over="ignore", invalid="ignore"):
+                        corr = np.where(m == -np.inf, 1.0, np.exp2(m - m_new))
+                    corr = np.where(fire, corr, 1.0)
+                    with np.errstate(over="ignore", invalid="ignore"):
+                        l = l * corr
+                        acc = acc * corr[:, None]
+                    m = np.where(fire, m_new, m)
+                # 3. exponentials against the (possibly stale) base, row sum of unrounded p
+                m_use = np.where(m == -np.inf, 0.0, m)
+                with np.errstate(over="ignore", invalid="ignore"):
+                    p = np.where(vis, np.exp2(st - m_use[:, None]), 0.0)
+                l = l + p.sum(axis=1)
+                # 4. P rounded to e4m3, then P . V with the raw fp8 values of V
+                pq = round_e4m3(p) if quantize_p else p
+                with np.errstate(over="ignore", invalid="ignore"):
+                    acc = acc + pq @ v8[b, cols, g, :]
+            m_use = np.where(m == -np.inf, 0.0, m)
+            ok = l > 0
+            with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+                out[b, :, h, :] = np.where(ok[:, None], acc * v_descale / np.where(ok, l, 1.0)[:, None], 0.0)
+                lse[b, h, :] = np.where(ok, (m_use + np.log2(np.where(ok, l, 1.0))) * _LN2, -np.inf)
+    if return_stats:
+        return out, lse, stats
+    return out, lse
