@@ -23,11 +23,11 @@ STATUS_NAMES = {
 }
 ERR_HIP = 11
 
-DTYPE_BF16, DTYPE_FP16 = 0, 1
+DTYPE_BF16, DTYPE_FP16, DTYPE_FP8_E4M3 = 0, 1, 2
 MASK_NONE, MASK_BOOL_U8, MASK_ADD_BF16 = 0, 1, 2
 
 EXPORTED = (
-    "exattn_abi_version", "exattn_check", "exattn_fwd", "exattn_bwd_workspace_size",
+    "exattn_abi_version", "exattn_check", "exattn_fwd", "exattn_fwd_fp8", "exattn_bwd_workspace_size",
     "exattn_bwd", "exattn_status_string", "exattn_last_error", "exattn_timing_enable",
     "exattn_timing_read", "exattn_set_variant",
 )
@@ -70,6 +70,8 @@ def load():
         lib.exattn_check.argtypes = [P]
         lib.exattn_fwd.restype = ctypes.c_int
         lib.exattn_fwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp]
+        lib.exattn_fwd_fp8.restype = ctypes.c_int
+        lib.exattn_fwd_fp8.argtypes = [P, _vp, _vp, _vp, _f32, _f32, _f32, _vp, _vp, _vp]
         lib.exattn_bwd_workspace_size.restype = ctypes.c_size_t
         lib.exattn_bwd_workspace_size.argtypes = [P]
         lib.exattn_bwd.restype = ctypes.c_int

@@ -19,7 +19,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["exattn_fwd", "exattn_bwd", "exattn_check", "attn_fwd", "attn_bwd", "attention",
+__all__ = ["exattn_fwd", "exattn_fwd_fp8", "exattn_bwd", "exattn_check", "attn_fwd", "attn_bwd", "attention",
            "AttnFunction", "timing_enable", "timing_read", "workspace_size", "set_variant"]
 
 
@@ -239,6 +239,65 @@ def exattn_fwd(q, k, v, *, causal=False, scale=None, mask=None, cu_seqlens_q=Non
             p = spec.problem(qn, kn, vn, side)
             st = lib.exattn_fwd(ctypes.byref(p), _ptr(qn), _ptr(kn), _ptr(vn), _ptr(out),
                                 _ptr(lse), ctypes.c_void_p(stream.cuda_stream))
+    if st != _lib.OK:
+        _fail(lib, st)
+    return out, lse
+
+
+def _norm_fp8(t: torch.Tensor) -> torch.Tensor:
+    """Head dim contiguous, other strides multiples of 16 elements, 16-byte aligned."""
+    ok = (t.stride(-1) == 1 and all(s % 16 == 0 for s in t.stride()[:-1])
+          and t.data_ptr() % 16 == 0)
+    return t if ok else t.contiguous()
+
+
+def exattn_fwd_fp8(q, k, v, q_descale=1.0, k_descale=1.0, v_descale=1.0, *, causal=False,
+                   scale=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fp8 forward: q [B, Sq, H, 128], k/v [B, Sk, Hkv, 128] as torch.float8_e4m3fn with one
+    descale per tensor (the represented values are q * q_descale, ...). Returns out
+    [B, Sq, H, 128] bf16 and lse [B, H, Sq] fp32 (natural log). The softmax walks key tiles
+    with a bounded rebase of its running max and rounds P to e4m3 for the P.V product (see
+    exattn_fwd_fp8 in include/exattn.h)."""
+    lib = _lib.load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a tensor")
+        if t.device.type != "cuda" or t.device != q.device:
+            raise ValueError(f"{name} must be on q's GPU device, got {t.device}")
+        if t.dtype != torch.float8_e4m3fn:
+            raise ValueError(f"{name} has dtype {t.dtype}; the fp8 forward takes torch.float8_e4m3fn")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [batch, seq, heads, head_dim]")
+    B, Sq, H, D = q.shape
+    Bk, Sk, Hkv, Dk = k.shape
+    if Bk != B or Dk != D or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shapes q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)} do not match")
+    if Hkv < 1 or H % Hkv != 0:
+        raise ValueError(f"heads_q={H} must be a multiple of heads_kv={Hkv}")
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    for name, x in (("scale", sc), ("q_descale", q_descale), ("k_descale", k_descale),
+                    ("v_descale", v_descale)):
+        if not math.isfinite(float(x)):
+            raise ValueError(f"{name} must be finite")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device)
+        with torch.cuda.stream(stream):
+            qn, kn, vn = _norm_fp8(q), _norm_fp8(k), _norm_fp8(v)
+            out = torch.empty((B, Sq, H, D), dtype=torch.bfloat16, device=q.device)
+            lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+            p = _lib.Problem()
+            p.dtype = _lib.DTYPE_FP8_E4M3
+            p.batch, p.seqlen_q, p.seqlen_k = B, Sq, Sk
+            p.heads_q, p.heads_kv, p.head_dim = H, Hkv, D
+            p.causal = int(bool(causal))
+            p.scale = sc
+            p.mask_kind = _lib.MASK_NONE
+            p.q_stride[:] = _strides3(qn, False)
+            p.k_stride[:] = _strides3(kn, False)
+            p.v_stride[:] = _strides3(vn, False)
+            st = lib.exattn_fwd_fp8(ctypes.byref(p), _ptr(qn), _ptr(kn), _ptr(vn),
+                                    float(q_descale), float(k_descale), float(v_descale),
+                                    _ptr(out), _ptr(lse), ctypes.c_void_p(stream.cuda_stream))
     if st != _lib.OK:
         _fail(lib, st)
     return out, lse

@@ -27,6 +27,7 @@ const char* kernel_name(KernelId id) {
     case KernelId::KvTail: return "exattn_bwd_kv_tail_kernel";
     case KernelId::QTail: return "exattn_bwd_q_tail_kernel";
     case KernelId::Zero: return "exattn_zero_kernel";
+    case KernelId::FwdFp8: return "exattn_fwd_fp8_kernel";
     default: return "unknown";
   }
 }
@@ -95,19 +96,34 @@ hipError_t timed(KernelId id, hipStream_t s, F&& f) {
 // ---- validation --------------------------------------------------------------------------
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-exattn_status check_strides(const int64_t* st, bool varlen, const char* name) {
+// Strides are in elements; rows must start on 16-byte boundaries (8 elements of 2 bytes,
+// 16 of 1 byte).
+exattn_status check_strides(const int64_t* st, bool varlen, const char* name, int mult) {
   for (int i = varlen ? 1 : 0; i < 3; ++i) {
-    if (st[i] < 0 || (st[i] & 7) != 0)
-      return fail(EXATTN_ERR_STRIDE, "%s stride[%d] = %lld must be a non-negative multiple of 8",
-                  name, i, (long long)st[i]);
+    if (st[i] < 0 || (st[i] % mult) != 0)
+      return fail(EXATTN_ERR_STRIDE, "%s stride[%d] = %lld must be a non-negative multiple of %d",
+                  name, i, (long long)st[i], mult);
   }
   return EXATTN_OK;
 }
 
-exattn_status validate(const exattn_problem* p, bool bwd) {
+// bwd: also check the out/dout strides. fp8: the problem of exattn_fwd_fp8 (e4m3 inputs,
+// head_dim 128, dense, no mask).
+exattn_status validate(const exattn_problem* p, bool bwd, bool fp8 = false) {
   if (!p) return fail(EXATTN_ERR_NULL, "problem pointer is NULL");
-  if (p->dtype != EXATTN_DTYPE_BF16 && p->dtype != EXATTN_DTYPE_FP16)
-    return fail(EXATTN_ERR_DTYPE, "dtype %d is not supported: bf16 (0) or fp16 (1)", p->dtype);
+  if (fp8) {
+    if (p->dtype != EXATTN_DTYPE_FP8_E4M3)
+      return fail(EXATTN_ERR_DTYPE, "dtype %d: the fp8 forward takes EXATTN_DTYPE_FP8_E4M3 (2)", p->dtype);
+    if (p->head_dim != 128)
+      return fail(EXATTN_ERR_HEAD_DIM, "head_dim %d: the fp8 forward supports 128 only", p->head_dim);
+    if (p->cu_seqlens_q || p->cu_seqlens_k)
+      return fail(EXATTN_ERR_VARLEN, "the fp8 forward takes dense (batch) inputs only");
+    if (p->mask_kind != EXATTN_MASK_NONE)
+      return fail(EXATTN_ERR_MASK, "the fp8 forward takes no mask (causal only)");
+  } else {
+    if (p->dtype != EXATTN_DTYPE_BF16 && p->dtype != EXATTN_DTYPE_FP16)
+      return fail(EXATTN_ERR_DTYPE, "dtype %d is not supported: bf16 (0) or fp16 (1)", p->dtype);
+  }
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(EXATTN_ERR_HEAD_DIM, "head_dim %d is not supported: only 64 and 128", p->head_dim);
   if (p->heads_q < 1 || p->heads_kv < 1 || p->heads_q % p->heads_kv != 0)
@@ -142,12 +158,13 @@ exattn_status validate(const exattn_problem* p, bool bwd) {
       return fail(EXATTN_ERR_ALIGN, "bf16 mask pointer must be 2-byte aligned");
   }
   exattn_status s;
-  if ((s = check_strides(p->q_stride, varlen, "q")) != EXATTN_OK) return s;
-  if ((s = check_strides(p->k_stride, varlen, "k")) != EXATTN_OK) return s;
-  if ((s = check_strides(p->v_stride, varlen, "v")) != EXATTN_OK) return s;
+  const int mult = fp8 ? 16 : 8;
+  if ((s = check_strides(p->q_stride, varlen, "q", mult)) != EXATTN_OK) return s;
+  if ((s = check_strides(p->k_stride, varlen, "k", mult)) != EXATTN_OK) return s;
+  if ((s = check_strides(p->v_stride, varlen, "v", mult)) != EXATTN_OK) return s;
   if (bwd) {
-    if ((s = check_strides(p->o_stride, varlen, "out")) != EXATTN_OK) return s;
-    if ((s = check_strides(p->do_stride, varlen, "dout")) != EXATTN_OK) return s;
+    if ((s = check_strides(p->o_stride, varlen, "out", 8)) != EXATTN_OK) return s;
+    if ((s = check_strides(p->do_stride, varlen, "dout", 8)) != EXATTN_OK) return s;
   }
   // Size limits: row counts times heads must index within int32 rows, blocks within 2^31.
   const int64_t rows_q = varlen ? (int64_t)p->seqlen_q : (int64_t)p->batch * p->seqlen_q;
@@ -220,7 +237,7 @@ int exattn_abi_version(void) { return EXATTN_ABI_VERSION; }
 
 exattn_status exattn_check(const exattn_problem* p) {
   g_err[0] = 0;
-  return validate(p, false);
+  return validate(p, false, p && p->dtype == EXATTN_DTYPE_FP8_E4M3);
 }
 
 const char* exattn_status_string(exattn_status s) {
@@ -304,6 +321,61 @@ exattn_status exattn_fwd(const exattn_problem* p, const void* q, const void* k, 
     e = timed(KernelId::FwdTail, s, [&] { return launch_fwd_tail(a, D, s); });
     if (e != hipSuccess) return hip_fail(e, "forward tail launch");
   }
+  return EXATTN_OK;
+}
+
+exattn_status exattn_fwd_fp8(const exattn_problem* p, const void* q, const void* k,
+                             const void* v, float q_descale, float k_descale, float v_descale,
+                             void* out, float* lse, void* stream) {
+  g_err[0] = 0;
+  exattn_status st = validate(p, false, true);
+  if (st != EXATTN_OK) return st;
+  // K and V tiles are read through 32-bit buffer offsets: 64 rows of the token stride.
+  if (p->k_stride[1] >= (1 << 24) || p->v_stride[1] >= (1 << 24))
+    return fail(EXATTN_ERR_STRIDE, "the fp8 forward needs k/v token strides below 2^24 elements");
+  if (!std::isfinite(q_descale) || !std::isfinite(k_descale) || !std::isfinite(v_descale))
+    return fail(EXATTN_ERR_SCALE, "descales must be finite");
+  const double c2 = (double)p->scale * q_descale * k_descale * 1.4426950408889634;
+  if (!std::isfinite((float)c2)) return fail(EXATTN_ERR_SCALE, "scale * q_descale * k_descale overflows");
+  const Geometry g = geometry(p);
+  const bool any = g.rows_q > 0 && p->heads_q > 0;
+  if (any && (!q || !out || !lse)) return fail(EXATTN_ERR_NULL, "q, out or lse is NULL");
+  if (any && g.rows_k > 0 && (!k || !v)) return fail(EXATTN_ERR_NULL, "k or v is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(EXATTN_ERR_ALIGN, "q/k/v/out must be 16-byte aligned and lse 4-byte aligned");
+  if (!any) return EXATTN_OK;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int D = p->head_dim, H = p->heads_q;
+  FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.q_sb = p->q_stride[0]; a.q_ss = p->q_stride[1]; a.q_sh = p->q_stride[2];
+  a.k_sb = p->k_stride[0]; a.k_ss = p->k_stride[1]; a.k_sh = p->k_stride[2];
+  a.v_sb = p->v_stride[0]; a.v_ss = p->v_stride[1]; a.v_sh = p->v_stride[2];
+  a.o_sh = D;  // out: contiguous bf16
+  a.o_ss = (int64_t)H * D;
+  a.o_sb = (int64_t)p->seqlen_q * H * D;
+  a.B = p->batch;
+  a.Sq = p->seqlen_q;
+  a.Sk = p->seqlen_k;
+  a.H = H;
+  a.Hkv = p->heads_kv;
+  a.group = H / p->heads_kv;
+  a.num_units = p->batch;
+  const int bm = fwd_fp8_block_m();
+  a.num_q_tiles = (p->seqlen_q + bm - 1) / bm;
+  a.lse_row = p->seqlen_q;
+  a.scale_log2 = (float)c2;
+  a.v_descale = v_descale;
+  if ((int64_t)a.num_units * H * a.num_q_tiles > INT32_MAX)
+    return fail(EXATTN_ERR_SHAPE, "too many query tiles");
+  hipError_t e = timed(KernelId::FwdFp8, s, [&] { return launch_fwd_fp8(a, p->causal != 0, s); });
+  if (e != hipSuccess) return hip_fail(e, "fp8 forward kernel launch");
   return EXATTN_OK;
 }
 

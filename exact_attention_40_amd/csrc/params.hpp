@@ -24,7 +24,8 @@ struct FwdArgs {
   int num_units;     // batch (dense) or num_seqs (packed)
   int num_q_tiles;   // per unit
   int lse_row;       // packed: row count of lse ([H, lse_row]); dense: Sq
-  float scale_log2;  // scale * log2(e)
+  float scale_log2;  // scale * log2(e); fp8 forward: scale * q_descale * k_descale * log2(e)
+  float v_descale;   // fp8 forward only: multiplies the normalised output
 };
 
 struct BwdArgs {
@@ -62,7 +63,7 @@ struct BwdArgs {
 };
 
 enum class KernelId : int {
-  Fwd = 0, FwdTail, Delta, BwdDkDv, BwdDq, BwdFused, DqReduce, KvTail, QTail, Zero, Count
+  Fwd = 0, FwdTail, Delta, BwdDkDv, BwdDq, BwdFused, DqReduce, KvTail, QTail, Zero, FwdFp8, Count
 };
 
 const char* kernel_name(KernelId id);
@@ -80,9 +81,11 @@ hipError_t launch_q_tail(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_dq_reduce(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_kv_tail(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_zero16(void* p, int64_t bytes, hipStream_t s);  // bytes % 16 == 0
+hipError_t launch_fwd_fp8(const FwdArgs& a, bool causal, hipStream_t s);  // head_dim 128, dense
 
 // Tile shapes the host needs for grid sizing, and the tiling selectors.
 int fwd_block_m(int head_dim, int mask, bool varlen);
+int fwd_fp8_block_m();
 void set_fwd_variant(int v);
 void set_bwd_variant(int v);
 int get_bwd_variant();

@@ -58,7 +58,7 @@ extern "C" {
 typedef enum exattn_status {
   EXATTN_OK = 0,
   EXATTN_ERR_NULL = 1,       /* a required pointer is NULL */
-  EXATTN_ERR_DTYPE = 2,      /* dtype is neither EXATTN_DTYPE_BF16 nor EXATTN_DTYPE_FP16 */
+  EXATTN_ERR_DTYPE = 2,      /* dtype not accepted by the call (bf16/fp16; fp8 e4m3 for fp8) */
   EXATTN_ERR_HEAD_DIM = 3,   /* head_dim not in {64, 128} */
   EXATTN_ERR_SHAPE = 4,      /* negative sizes, heads_q % heads_kv != 0, size overflow */
   EXATTN_ERR_STRIDE = 5,     /* a stride is negative or not a multiple of 8 elements */
@@ -66,15 +66,21 @@ typedef enum exattn_status {
   EXATTN_ERR_MASK = 7,       /* bad mask kind, NULL mask, negative mask stride, mask + varlen */
   EXATTN_ERR_VARLEN = 8,     /* num_seqs < 1, max_seqlen < 0, or one cu_seqlens pointer NULL */
   EXATTN_ERR_WORKSPACE = 9,  /* workspace NULL, too small or not 256-byte aligned */
-  EXATTN_ERR_SCALE = 10,     /* scale is NaN or infinite */
+  EXATTN_ERR_SCALE = 10,     /* scale (or an fp8 descale) is NaN or infinite */
   EXATTN_ERR_HIP = 11        /* a HIP launch failed; see exattn_last_error() */
 } exattn_status;
 
 /* Element type of q, k, v, out, dout, dq, dk, dv (all the same). fp16 is threaded through
  * every kernel instead of being rejected (cudnn-frontend PR #429, the fp16 follow-up
  * commit: the element type reaches the kernel rather than being hard-coded). Additive
- * masks are bf16 for either type. */
-typedef enum exattn_dtype { EXATTN_DTYPE_BF16 = 0, EXATTN_DTYPE_FP16 = 1 } exattn_dtype;
+ * masks are bf16 for either type. EXATTN_DTYPE_FP8_E4M3 (OCP e4m3: 4 exponent bits, bias
+ * 7, 3 mantissa bits, largest finite 448) is the input type of exattn_fwd_fp8 only; its
+ * output is bf16. */
+typedef enum exattn_dtype {
+  EXATTN_DTYPE_BF16 = 0,
+  EXATTN_DTYPE_FP16 = 1,
+  EXATTN_DTYPE_FP8_E4M3 = 2
+} exattn_dtype;
 
 typedef enum exattn_mask_kind {
   EXATTN_MASK_NONE = 0,
@@ -146,6 +152,28 @@ exattn_status exattn_check(const exattn_problem* p);
 exattn_status exattn_fwd(const exattn_problem* p, const void* q, const void* k,
                          const void* v, void* out, float* lse, void* stream);
 
+/*
+ * fp8 forward (FlyDSL PR #1033, "[Bugfix][Kernel] Fix NaN from the lazy rescale on a wide
+ * score range", section "The fp8 helper, second commit"). q, k, v: device e4m3 bytes in the
+ * dense layout above (p->dtype = EXATTN_DTYPE_FP8_E4M3, head_dim 128, no mask, no
+ * cu_seqlens; strides multiples of 16 elements), each with one float descale: the
+ * represented values are q * q_descale and so on. The softmax sees the scores
+ * s_ij = q_i . k_j * scale * q_descale * k_descale. Key tiles of 64 are walked in order
+ * with a running base per query row: when, in a group of 32 consecutive rows (one
+ * 64-wide wave), some row's tile max exceeds its base by more than 8 (log2 units), every
+ * row of the group is rebased onto its own tile max, but never more than 16 (log2 units)
+ * below the row's running max; exponentials against the base (at most 2^8) are rounded to
+ * e4m3 for the product with v, the row sum takes them unrounded. out (bf16, written
+ * contiguous [batch, seqlen_q, heads_q, 128]) is (rounded P) v * v_descale / row sum, so it
+ * differs from exact attention of the represented values by the e4m3 rounding of P; lse
+ * (fp32 [batch, heads_q, seqlen_q], natural log) is the exact log-sum-exp up to fp32
+ * rounding. Rows with no visible key get out = 0, lse = -inf. Descales must be finite
+ * (EXATTN_ERR_SCALE otherwise); errors as for exattn_fwd.
+ */
+exattn_status exattn_fwd_fp8(const exattn_problem* p, const void* q, const void* k,
+                             const void* v, float q_descale, float k_descale, float v_descale,
+                             void* out, float* lse, void* stream);
+
 /* Bytes of device workspace exattn_bwd needs for this problem under the backward variant
  * selected at the time of the call (see exattn_set_variant; 0 on invalid input). */
 size_t exattn_bwd_workspace_size(const exattn_problem* p);
@@ -190,7 +218,7 @@ int exattn_timing_read(const char** names, double* total_ms, int* launches, int 
  * Tiling selection, for benchmarking the compiled alternatives. `kernel` 0 = forward:
  * variant 0 (default) = 8 waves x 32 query rows per workgroup with the lazy rescale
  * (threshold 8 in log2 units), 1 = the same tiling with an eager rescale whenever a row
- * max grows, 2 = 4 waves x 32 rows (lazy), two workgroups per compute unit; 2 applies to
+ * max grows, 2 = 4 waves x 64 rows (lazy), one wave per SIMD; 2 applies to
  * head_dim 128 without a mask or cu_seqlens, other problems fall back to 0. `kernel` 1 =
  * backward:
  * 0 (default) = a dK/dV kernel (one workgroup per block of keys) and a separate dQ kernel

@@ -15,10 +15,10 @@ oracle walks the key tiles in order):
 * when the wave-wide test fires, a row does not keep max(m_row, m_tile): it is rebased
   onto its own tile max even when that is lower than the running max, which keeps the
   exponentials of the current tile near 1 where fp8 resolves them best;
-* the fix caps how far one rebase may lower the base at 16 (log2 units), so the factor
-  applied to the row's accumulators is at most 2**16. Without the cap a row dragged along
-  by another row's rise multiplies its sums by 2**(m_row - m_tile), which overflows on a
-  wide score range (the NaN the section reports).
+* the fix caps how far the base may fall at 16 (log2 units), so the factor applied to the
+  row's accumulators is at most 2**16. Without the cap a row dragged along by another
+  row's rise multiplies its sums by 2**(m_row - m_tile), which overflows on a wide score
+  range (the NaN the section reports).
 
 Readings where the section is silent (each is listed in the design notes):
 
@@ -31,7 +31,13 @@ Readings where the section is silent (each is listed in the design notes):
 * the wave-wide test covers `group_rows` consecutive query rows (32 on the GPU: one row
   per lane pair of a 64-wide wave), the key tile is `block_n` keys (64 on the GPU);
 * a row with no visible key so far keeps m = -inf, its factor is taken as 1 (its sums are
-  zero), and lse = (m + log2 l) * ln 2 is the natural-log LSE of the bf16 path.
+  zero), and lse = (m + log2 l) * ln 2 is the natural-log LSE of the bf16 path;
+* the cap is measured from the row's running max M (the largest visible scaled score seen
+  so far): a rebase sets the base to max(m_tile, M - 16). Then the base never sits more
+  than 16 below M, and the sums never exceed 2**16 times their max-based values. Capping
+  each rebase against the previous base instead lets drops compound when other rows keep
+  firing (eight capped drops already exceed the fp32 range); the two readings agree
+  whenever a row's base never falls more than 16 below its running max.
 """
 
 from __future__ import annotations
@@ -65,16 +71,18 @@ def round_e4m3(x):
 
 def fp8_forward(q8, k8, v8, q_descale, k_descale, v_descale, *, causal=False, scale=None,
                 block_n=64, group_rows=32, tau=8.0, bound=16.0, quantize_p=True,
-                return_stats=False):
+                return_stats=False, units=None, row_groups=None):
     """fp8 attention forward, tile by tile as the FlyDSL fp8 helper does (see module doc).
 
     q8 [B, Sq, H, D], k8 / v8 [B, Sk, Hkv, D]: float arrays holding e4m3 values (decoded,
     without their descales). Returns out [B, Sq, H, D] and lse [B, H, Sq] in float64.
-    ``bound=None`` rebases without a cap (the behaviour before the fix);
+    ``bound=None`` rebases onto the tile max without a cap (the behaviour before the fix);
     ``quantize_p=False`` skips the e4m3 rounding of P (then the result is the exact
     attention of the dequantised inputs, whatever the rebase sequence).
     With ``return_stats`` a dict counts triggered tiles and rebases that lowered a base,
-    and those the cap limited.
+    and those the cap limited. ``units`` (a list of (b, h)) and ``row_groups`` (indices of
+    groups of ``group_rows`` rows) restrict the work; entries left out are NaN. A group's
+    rows share every decision, so a group is computed whole or not at all.
     """
     q8, k8, v8 = (np.asarray(t, dtype=np.float64) for t in (q8, k8, v8))
     B, Sq, H, D = q8.shape
@@ -82,59 +90,69 @@ def fp8_forward(q8, k8, v8, q_descale, k_descale, v_descale, *, causal=False, sc
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     c2 = scale * q_descale * k_descale * _LOG2E          # logit scale, log2 units
-    out = np.zeros((B, Sq, H, D))
-    lse = np.full((B, H, Sq), -np.inf)
+    subset = units is not None or row_groups is not None
+    out = np.full((B, Sq, H, D), np.nan if subset else 0.0)
+    lse = np.full((B, H, Sq), np.nan if subset else -np.inf)
     stats = {"triggers": 0, "lowered": 0, "capped": 0}
-    group = np.arange(Sq) // group_rows
-    for b in range(B):
-        for h in range(H):
-            g = h // (H // Hkv)
-            s2 = (q8[b, :, h, :] @ k8[b, :, g, :].T) * c2          # [Sq, Sk]
-            m = np.full(Sq, -np.inf)
-            l = np.zeros(Sq)
-            acc = np.zeros((Sq, D))
-            for j0 in range(0, Sk, block_n):
-                cols = np.arange(j0, min(j0 + block_n, Sk))
-                vis = np.ones((Sq, cols.size), dtype=bool)
-                if causal:
-                    vis &= cols[None, :] <= np.arange(Sq)[:, None]
-                st = np.where(vis, s2[:, cols], -np.inf)
-                m_tile = st.max(axis=1)
-                # 1. rescale test per row (a row with m = -inf and a visible key fires:
-                #    +inf > tau), then made common to each group of rows
-                with np.errstate(invalid="ignore"):
-                    fire_row = (m_tile - m) > tau
-                fire_grp = np.zeros(group.max() + 1, dtype=bool)
-                np.logical_or.at(fire_grp, group, fire_row)
-                fire = fire_grp[group]
-                # 2. rebase: onto the row's tile max, lowering the base by at most `bound`
-                if fire.any():
-                    stats["triggers"] += int(fire_grp.sum())
-                    m_new = m_tile if bound is None else np.maximum(m_tile, m - bound)
-                    stats["lowered"] += int(np.sum(fire & (m_new < m)))
-                    if bound is not None:
-                        stats["capped"] += int(np.sum(fire & (m_tile < m - bound)))
-                    with np.errstate(over="ignore", invalid="ignore"):
-                        corr = np.where(m == -np.inf, 1.0, np.exp2(m - m_new))
-                    corr = np.where(fire, corr, 1.0)
-                    with np.errstate(over="ignore", invalid="ignore"):
-                        l = l * corr
-                        acc = acc * corr[:, None]
-                    m = np.where(fire, m_new, m)
-                # 3. exponentials against the (possibly stale) base, row sum of unrounded p
-                m_use = np.where(m == -np.inf, 0.0, m)
+    if row_groups is None:
+        rows = np.arange(Sq)
+    else:
+        rows = np.concatenate([np.arange(gi * group_rows, min((gi + 1) * group_rows, Sq))
+                               for gi in row_groups])
+    n = rows.size
+    group = np.unique(rows // group_rows, return_inverse=True)[1].reshape(-1)
+    todo = units if units is not None else [(b, h) for b in range(B) for h in range(H)]
+    for (b, h) in todo:
+        g = h // (H // Hkv)
+        s2 = (q8[b, rows, h, :] @ k8[b, :, g, :].T) * c2       # [n, Sk]
+        m = np.full(n, -np.inf)        # base of the exponentials
+        m_max = np.full(n, -np.inf)    # running max of the visible scaled scores
+        l = np.zeros(n)
+        acc = np.zeros((n, D))
+        for j0 in range(0, Sk, block_n):
+            cols = np.arange(j0, min(j0 + block_n, Sk))
+            vis = np.ones((n, cols.size), dtype=bool)
+            if causal:
+                vis &= cols[None, :] <= rows[:, None]
+            st = np.where(vis, s2[:, cols], -np.inf)
+            m_tile = st.max(axis=1)
+            m_max = np.maximum(m_max, m_tile)
+            # 1. rescale test per row (a row with m = -inf and a visible key fires:
+            #    +inf > tau), then made common to each group of rows
+            with np.errstate(invalid="ignore"):
+                fire_row = (m_tile - m) > tau
+            fire_grp = np.zeros(group.max() + 1, dtype=bool)
+            np.logical_or.at(fire_grp, group, fire_row)
+            fire = fire_grp[group]
+            # 2. rebase: onto the row's tile max, never more than `bound` below its
+            #    running max
+            if fire.any():
+                stats["triggers"] += int(fire_grp.sum())
+                m_new = m_tile if bound is None else np.maximum(m_tile, m_max - bound)
+                stats["lowered"] += int(np.sum(fire & (m_new < m)))
+                if bound is not None:
+                    stats["capped"] += int(np.sum(fire & (m_tile < m_max - bound)))
                 with np.errstate(over="ignore", invalid="ignore"):
-                    p = np.where(vis, np.exp2(st - m_use[:, None]), 0.0)
-                l = l + p.sum(axis=1)
-                # 4. P rounded to e4m3, then P . V with the raw fp8 values of V
-                pq = round_e4m3(p) if quantize_p else p
+                    corr = np.where(m == -np.inf, 1.0, np.exp2(m - m_new))
+                corr = np.where(fire, corr, 1.0)
                 with np.errstate(over="ignore", invalid="ignore"):
-                    acc = acc + pq @ v8[b, cols, g, :]
+                    l = l * corr
+                    acc = acc * corr[:, None]
+                m = np.where(fire, m_new, m)
+            # 3. exponentials against the (possibly stale) base, row sum of unrounded p
             m_use = np.where(m == -np.inf, 0.0, m)
-            ok = l > 0
-            with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
-                out[b, :, h, :] = np.where(ok[:, None], acc * v_descale / np.where(ok, l, 1.0)[:, None], 0.0)
-                lse[b, h, :] = np.where(ok, (m_use + np.log2(np.where(ok, l, 1.0))) * _LN2, -np.inf)
+            with np.errstate(over="ignore", invalid="ignore"):
+                p = np.where(vis, np.exp2(st - m_use[:, None]), 0.0)
+            l = l + p.sum(axis=1)
+            # 4. P rounded to e4m3, then P . V with the raw fp8 values of V
+            pq = round_e4m3(p) if quantize_p else p
+            with np.errstate(over="ignore", invalid="ignore"):
+                acc = acc + pq @ v8[b, cols, g, :]
+        m_use = np.where(m == -np.inf, 0.0, m)
+        ok = l > 0
+        with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+            out[b, rows, h, :] = np.where(ok[:, None], acc * v_descale / np.where(ok, l, 1.0)[:, None], 0.0)
+            lse[b, h, rows] = np.where(ok, (m_use + np.log2(np.where(ok, l, 1.0))) * _LN2, -np.inf)
     if return_stats:
         return out, lse, stats
     return out, lse

@@ -24,7 +24,7 @@ def lib():
 def _declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(exattn_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(exattn_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -96,7 +96,7 @@ def test_check_accepts_valid_problem(lib):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dtype=2), 2),                        # an unknown dtype is rejected, not run as bf16
+    (dict(dtype=3), 2),                        # an unknown dtype is rejected, not run as bf16
     (dict(dtype=-1), 2),
     (dict(head_dim=96), 3),                    # only 64 and 128
     (dict(head_dim=256), 3),
@@ -127,6 +127,36 @@ def test_check_rejects(lib, kw, status):
     assert lib.exattn_bwd(ctypes.byref(p), 16, 16, 16, 16, 16, 16, 16, 16, 16, 256, 1 << 30,
                           None) == status
     assert lib.exattn_bwd_workspace_size(ctypes.byref(p)) == 0
+
+
+def _fp8(**kw):
+    return _problem(**{"dtype": 2, **kw})
+
+
+def _fwd_fp8(lib, p, q=16, k=16, v=16, ds=(1.0, 1.0, 1.0), out=16, lse=16):
+    return lib.exattn_fwd_fp8(ctypes.byref(p), q, k, v, *ds, out, lse, None)
+
+
+def test_fp8_forward_validation(lib):
+    assert lib.exattn_check(ctypes.byref(_fp8())) == 0
+    # the 16-bit entry points reject e4m3 problems, the fp8 one rejects 16-bit problems
+    assert lib.exattn_fwd(ctypes.byref(_fp8()), 16, 16, 16, 16, 16, None) == 2
+    assert lib.exattn_bwd(ctypes.byref(_fp8()), *([16] * 9), 256, 1 << 30, None) == 2
+    assert _fwd_fp8(lib, _problem()) == 2
+    assert _fwd_fp8(lib, _fp8(head_dim=64, q_stride=(100 * 256, 256, 64), k_stride=(77 * 128, 128, 64),
+                              v_stride=(77 * 128, 128, 64))) == 3
+    assert _fwd_fp8(lib, _fp8(mask_kind=1, mask=16)) == 7
+    assert _fwd_fp8(lib, _fp8(cu_seqlens_q=4096, cu_seqlens_k=4096, num_seqs=1, max_seqlen_q=10,
+                              max_seqlen_k=10)) == 8
+    assert _fwd_fp8(lib, _fp8(q_stride=(100 * 520, 520, 136))) == 5   # multiple of 8, not 16
+    assert _fwd_fp8(lib, _fp8(k_stride=(0, 1 << 24, 128))) == 5
+    assert _fwd_fp8(lib, _fp8(), ds=(float("inf"), 1.0, 1.0)) == 10
+    assert _fwd_fp8(lib, _fp8(), ds=(1.0, 1.0, float("nan"))) == 10
+    assert _fwd_fp8(lib, _fp8(), ds=(1e30, 1e30, 1.0)) == 10          # logit scale overflows
+    assert _fwd_fp8(lib, _fp8(), q=None) == 1
+    assert _fwd_fp8(lib, _fp8(), q=24) == 6
+    assert _fwd_fp8(lib, _fp8(), lse=18) == 6
+    assert _fwd_fp8(lib, _fp8(batch=0), q=None, k=None, v=None, out=None, lse=None) == 0
 
 
 def test_null_and_alignment_rejected_before_launch(lib):

@@ -1,0 +1,144 @@
+"""fp8 forward with a bounded rebase (FlyDSL PR #1033, "The fp8 helper, second commit")
+against its float64 oracle (oracle/fp8.py), which walks the same key tiles (64 keys) with the
+same wave-wide decisions (groups of 32 rows) and rounds P to e4m3 the same way.
+
+Two kinds of input:
+* "grid" values (q, k in {0, +-0.5, ..., +-2}, v in {+-0.5, +-1}): every product and dot
+  product is exact in fp32, so the GPU's scores equal the oracle's up to one rounding of
+  the logit scale; what remains is the bf16 rounding of out and rare e4m3 ties of P.
+* quantised normals: the fp8 MFMA's own accumulation error (about 1e-4 of sum |a_k b_k| on
+  random e4m3 operands) moves scores slightly, which now and then moves an exponential
+  across an e4m3 rounding boundary (one e4m3 step is 1/16 to 1/8 relative). Measured
+  out rel-L2 is 1.7e-3 to 2.2e-3 (bf16 output rounding alone gives about 1.1e-3); the
+  bar leaves a factor of about 3.
+Both are also checked against exact attention of the dequantised inputs: the fp8 result
+must stay within the e4m3 rounding of P (a few percent), far from an unrelated answer.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_40_amd import api, workloads
+from gpu_util import nonfinite, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+TOL_GRID = dict(out=5e-3, lse=1e-5)
+TOL_NORMAL = dict(out=6e-3, lse=2e-5)
+TOL_EXACT = 0.07
+
+
+def _run(p, scale=None):
+    q, k, v = p.q.cuda(), p.k.cuda(), p.v.cuda()
+    out, lse = api.exattn_fwd_fp8(q, k, v, p.q_descale, p.k_descale, p.v_descale,
+                                  causal=p.causal, scale=scale)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _check(p, tol, tag, scale=None, units=None, row_groups=None):
+    out, lse = _run(p, scale)
+    assert out.dtype == torch.bfloat16 and nonfinite(out) == 0, tag
+    q, k, v = p.decoded()
+    ro, rl, st = oracle.fp8_forward(q, k, v, p.q_descale, p.k_descale, p.v_descale,
+                                    causal=p.causal, scale=scale, units=units,
+                                    row_groups=row_groups, return_stats=True)
+    go, gl = out.float().cpu().numpy(), lse.cpu().numpy()
+    sel_o, sel_l = ~np.isnan(ro), ~np.isnan(rl)
+    finite = np.isfinite(rl) & sel_l
+    assert np.array_equal(np.isneginf(gl[sel_l]), np.isneginf(rl[sel_l])), tag
+    e_out = rel_l2(go[sel_o], ro[sel_o])
+    e_lse = rel_l2(gl[finite], rl[finite])
+    say(f"[fp8 {tag}] out rel-L2 {e_out:.3e}  lse rel-L2 {e_lse:.3e}  stats {st}")
+    assert e_out <= tol["out"], f"{tag}: out rel-L2 {e_out:.3e}"
+    assert e_lse <= tol["lse"], f"{tag}: lse rel-L2 {e_lse:.3e}"
+    return go, gl, ro, st
+
+
+GRID = [
+    dict(name="grid_s300", args=(1, 300, 300, 2, 1, 128), causal=False, km=1.0),
+    dict(name="grid_causal_gqa", args=(2, 257, 193, 4, 2, 128), causal=True, km=1.0),
+    dict(name="grid_long_k", args=(1, 64, 1000, 2, 2, 128), causal=False, km=1.0),
+    dict(name="grid_wide_cap", args=(1, 200, 700, 2, 1, 128), causal=False, km=6.0),
+    dict(name="grid_causal_tail", args=(1, 513, 513, 1, 1, 128), causal=True, km=0.5),
+]
+
+
+@pytest.mark.parametrize("case", GRID, ids=[c["name"] for c in GRID])
+def test_fp8_grid_parity(case):
+    p = workloads.fp8_dense(*case["args"], seed=9100, causal=case["causal"], kind="grid",
+                            k_mult=case["km"])
+    _, _, _, st = _check(p, TOL_GRID, case["name"])
+    if case["name"] == "grid_wide_cap":
+        assert st["capped"] > 0       # the bound was exercised
+
+
+NORMAL = [
+    dict(name="normal_s640", args=(1, 640, 640, 2, 1, 128), causal=False, km=1.0),
+    dict(name="normal_causal", args=(1, 700, 700, 2, 2, 128), causal=True, km=1.0),
+    dict(name="normal_k32", args=(1, 300, 900, 2, 1, 128), causal=False, km=32.0),
+]
+
+
+@pytest.mark.parametrize("case", NORMAL, ids=[c["name"] for c in NORMAL])
+def test_fp8_normal_parity_and_distance_from_exact(case):
+    p = workloads.fp8_dense(*case["args"], seed=9200, causal=case["causal"], k_mult=case["km"])
+    go, _, _, _ = _check(p, TOL_NORMAL, case["name"])
+    q, k, v = p.decoded()
+    eo, _ = oracle.attention_forward(q * p.q_descale, k * p.k_descale, v * p.v_descale,
+                                     causal=case["causal"])
+    e = rel_l2(go, eo)
+    say(f"[fp8 {case['name']}] vs exact attention of the dequantised inputs: {e:.3e}")
+    assert e < TOL_EXACT
+
+
+def test_fp8_negative_scale_and_value_ones():
+    p = workloads.fp8_dense(1, 200, 333, 2, 1, 128, seed=9300, kind="grid", v_ones=True)
+    go, _, _, _ = _check(p, TOL_GRID, "negative_scale", scale=-1.0 / math.sqrt(128))
+    # V = ones: out = sum(e4m3(p)) / sum(p), off 1 only by the rounding of P (at most 1/16
+    # per element; the oracle's own mean is 3.5e-3 here)
+    assert np.abs(go - 1.0).mean() < 5e-3 and np.abs(go - 1.0).max() < 0.0625
+
+
+def test_fp8_no_keys_and_single_key():
+    p = workloads.fp8_dense(1, 40, 1, 2, 1, 128, seed=9301, kind="grid")
+    out, lse = _run(p)
+    q, k, v = p.decoded()
+    assert torch.equal(out[0, :, 0].float().cpu(), torch.from_numpy(v[0, 0, 0]).float().expand(40, 128))
+    p0 = workloads.fp8_dense(1, 40, 0, 2, 1, 128, seed=9302, kind="grid")
+    out0, lse0 = _run(p0)
+    assert torch.count_nonzero(out0).item() == 0
+    assert torch.all(torch.isneginf(lse0)).item()
+
+
+def test_fp8_rejects_other_inputs():
+    p = workloads.fp8_dense(1, 64, 64, 2, 1, 64, seed=9303, kind="grid")
+    with pytest.raises(ValueError, match="HEAD_DIM"):
+        _run(p)
+    q = torch.zeros(1, 64, 2, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="float8_e4m3fn"):
+        api.exattn_fwd_fp8(q, q, q)
+    p = workloads.fp8_dense(1, 64, 64, 2, 1, 128, seed=9304, kind="grid")
+    with pytest.raises(ValueError, match="finite"):
+        api.exattn_fwd_fp8(p.q.cuda(), p.k.cuda(), p.v.cuda(), float("inf"), 1.0, 1.0)
+
+
+def test_fp8_full_size_sampled():
+    """B=2 S=8192 H=32 D=128 non-causal, the launch the benchmark times: sampled row groups
+    of two heads against the oracle, every element finite."""
+    p = workloads.fp8_dense(2, 8192, 8192, 32, 32, 128, seed=9400)
+    out, lse = _run(p)
+    assert nonfinite(out) == 0 and nonfinite(lse) == 0
+    q, k, v = p.decoded()
+    ro, rl = oracle.fp8_forward(q, k, v, p.q_descale, p.k_descale, p.v_descale,
+                                units=[(0, 0), (1, 31)], row_groups=[0, 131, 255])
+    sel = ~np.isnan(ro)
+    go, gl = out.float().cpu().numpy(), lse.cpu().numpy()
+    e_out = rel_l2(go[sel], ro[sel])
+    e_lse = rel_l2(gl[~np.isnan(rl)], rl[~np.isnan(rl)])
+    say(f"[fp8 full size sampled] out rel-L2 {e_out:.3e}  lse rel-L2 {e_lse:.3e}")
+    assert e_out <= TOL_NORMAL["out"] and e_lse <= TOL_NORMAL["lse"]

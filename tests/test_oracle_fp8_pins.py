@@ -118,7 +118,7 @@ def test_uncapped_rebase_overflows_capped_does_not():
     # Two rows share one rescale decision. Row 0's scores rise by 100 (log2 units) per key
     # tile, so it fires on every tile; row 1 peaks in tile 0 and then falls 3000 below.
     # Uncapped, row 1 is rebased onto that low tile max and its sums are multiplied by
-    # 2^3000 (inf); capped, each rebase lowers its base by 16 at most.
+    # 2^3000 (inf); capped, its base stays within 16 of its running max (0).
     D, n = 4, 4
     ntile = 3
     Sk = n * ntile
@@ -136,7 +136,7 @@ def test_uncapped_rebase_overflows_capped_does_not():
         o_free, _ = fp8_forward(q, k, v, 1.0, c, 1.0, bound=None, **kw)
     o_cap, l_cap, st = fp8_forward(q, k, v, 1.0, c, 1.0, bound=16.0, return_stats=True, **kw)
     assert not np.all(np.isfinite(o_free[0, 1]))
-    assert np.all(np.isfinite(o_cap)) and st["capped"] == 2
+    assert np.all(np.isfinite(o_cap)) and st["capped"] == 2 and st["lowered"] == 1
     assert np.allclose(o_cap, 1.0, rtol=0, atol=1e-12)      # V = ones: out = 1 exactly
     assert abs(l_cap[0, 0, 1] - (math.log(n) + 0.0)) < 1e-9  # row 1: lse = ln(4 e^0 + tiny)
 
@@ -158,3 +158,35 @@ def test_value_ones_output_near_one(k_mult):
     out, _ = fp8_forward(q, k, v, p.q_descale, p.k_descale, p.v_descale)
     assert np.all(np.isfinite(out))
     assert np.mean(np.abs(out - 1.0)) < 5e-3
+
+
+def test_subsets_match_the_whole():
+    p = workloads.fp8_dense(2, 100, 130, 2, 1, 16, seed=36, causal=True, k_mult=20.0)
+    q, k, v = p.decoded()
+    kw = dict(causal=True, block_n=32, group_rows=32)
+    out, lse = fp8_forward(q, k, v, p.q_descale, p.k_descale, p.v_descale, **kw)
+    so, sl = fp8_forward(q, k, v, p.q_descale, p.k_descale, p.v_descale, units=[(1, 0)],
+                         row_groups=[0, 3], **kw)
+    rows = np.r_[0:32, 96:100]
+    assert np.array_equal(so[1, rows, 0], out[1, rows, 0])
+    assert np.array_equal(sl[1, 0, rows], lse[1, 0, rows])
+    assert np.all(np.isnan(so[0])) and np.all(np.isnan(so[1, 32:96, 0]))
+
+
+def test_cap_bounds_the_base_below_the_running_max():
+    """Rows firing in turn must not drag a quiet row's base ever lower: with one row rising
+    on every tile and the other far below its own max, the quiet row's base falls once, by
+    16, and its sums stay within 2^16 of their max-based values (finite in fp32 terms)."""
+    D, n, ntile = 4, 4, 40
+    Sk = n * ntile
+    q = np.zeros((1, 2, 1, D)); q[0, 0, 0, 0] = 1.0; q[0, 1, 0, 1] = 1.0
+    k = np.zeros((1, Sk, 1, D))
+    for t in range(ntile):
+        k[0, t * n:(t + 1) * n, 0, 0] = 20.0 * t           # row 0 fires on every tile
+        k[0, t * n:(t + 1) * n, 0, 1] = 0.0 if t == 0 else -500.0
+    c = math.sqrt(D) * math.log(2.0)
+    out, lse, st = fp8_forward(q, k, np.ones((1, Sk, 1, D)), 1.0, c, 1.0, block_n=n,
+                               group_rows=2, quantize_p=False, return_stats=True)
+    assert st["triggers"] == ntile and st["lowered"] == 1
+    assert np.allclose(out, 1.0, rtol=0, atol=1e-12)
+    assert abs(lse[0, 0, 1] - math.log(n)) < 1e-9
