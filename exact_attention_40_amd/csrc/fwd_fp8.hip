@@ -21,7 +21,10 @@
 // Work decomposition: one workgroup = 8 waves = one (batch, head, 256-row query tile);
 // each wave owns 32 query rows (lane l and l ^ 32 share a row and split its keys). K and V
 // tiles of 64 keys x 128 bytes are copied straight into LDS (buffer loads with an LDS
-// destination, zero past the last key), double-buffered.
+// destination, zero past the last key), K one tile further ahead than V.
+// Software pipeline: iteration t issues the S MFMAs of tile t+1 next to the exponentials
+// of tile t, then the PV MFMAs of tile t next to the row max of tile t+1; the rescale test
+// for tile t+1 follows, outside the interleaved region.
 //   S^T = K Q^T: 32x32x64 fp8 MFMAs, A = K rows from LDS (32 contiguous bytes per lane),
 //     B = Q^T from registers; a lane's accumulators hold one query column.
 //   O^T += V^T P^T: A = V^T from transposed byte reads of the row-major V tile
@@ -30,6 +33,8 @@
 // gives them: byte j of lane-half h is key 32*(j/16) + 8*((j%16)/4) + 4*h + j%4, and the
 // transposed V reads fetch the same keys (read t of 8 bytes covers keys 16t + {4h..4h+3,
 // 8+4h..8+4h+3}).
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "params.hpp"
@@ -170,15 +175,40 @@ fwd_fp8_kernel(FwdArgs a) {
     if (CAUSAL) n_plain = min(n_plain, (qt0 + 1) / T::BN);
     n_plain = min(n_plain, ntiles);
 
-    auto load_kv = [&](int t, int buf) {
+    auto load_k = [&](int t, int buf) {
       const int kb0 = t * T::BN;
       const int rows = min(T::BN, Sk - kb0);
       copy_fp8_tile<false>(smem + buf * T::TB,
                            make_rsrc(K + (int64_t)kb0 * a.k_ss, (uint32_t)((rows - 1) * a.k_ss + T::D)),
                            a.k_ss, wave, lane);
+    };
+    auto load_v = [&](int t, int buf) {
+      const int kb0 = t * T::BN;
+      const int rows = min(T::BN, Sk - kb0);
       copy_fp8_tile<true>(smem + V_OFF + buf * T::TB,
                           make_rsrc(V + (int64_t)kb0 * a.v_ss, (uint32_t)((rows - 1) * a.v_ss + T::D)),
                           a.v_ss, wave, lane);
+    };
+    // Key kj visible to this lane's row (tiles that need masking only).
+    auto visible = [&](int kj) -> bool {
+      bool vis = kj < Sk && qi < Sq;
+      if (CAUSAL) vis = vis && kj <= qi;
+      return vis;
+    };
+    // K fragment i = 2*kk + st (k-chunk kk, keys 32st..32st+31) of the tile at byte kofs.
+    auto kfrag = [&](int kofs, int i) -> i32x8 {
+      const u32x4 lo = lds_at<u32x4>(kb[i >> 1][0], kofs + (i & 1) * 32 * T::RB);
+      const u32x4 hi = lds_at<u32x4>(kb[i >> 1][1], kofs + (i & 1) * 32 * T::RB);
+      return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    };
+    // V^T fragment of d-block db of the V tile at byte vofs: four transposed 8-byte reads.
+    auto vfrag = [&](int vofs, int db) -> i32x8 {
+      const i32x2 r0 = lds_read_tr8(vb[db] + vofs + 0 * 16 * T::RB);
+      const i32x2 r1 = lds_read_tr8(vb[db] + vofs + 1 * 16 * T::RB);
+      const i32x2 r2 = lds_read_tr8(vb[db] + vofs + 2 * 16 * T::RB);
+      const i32x2 r3 = lds_read_tr8(vb[db] + vofs + 3 * 16 * T::RB);
+      return i32x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
     };
 
     f32x16 o[4];
@@ -186,51 +216,10 @@ fwd_fp8_kernel(FwdArgs a) {
     for (int db = 0; db < 4; ++db) o[db] = f32x16{};
     float m_run = -INFINITY, m_max = -INFINITY, l_run = 0.f;   // base, running max, sum
 
-    if (ntiles > 0) load_kv(0, 0);
-    wait_vmem();
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-      const int buf = t & 1;
-      if (t + 1 < ntiles) load_kv(t + 1, buf ^ 1);
-      const int kofs = buf * T::TB;
-
-      // S^T for keys 64t + 32st + row, this lane's query column
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const u32x4 lo = lds_at<u32x4>(kb[kk][0], kofs + st * 32 * T::RB);
-          const u32x4 hi = lds_at<u32x4>(kb[kk][1], kofs + st * 32 * T::RB);
-          const i32x8 kf = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                            (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          s[st] = mfma32_e4m3(kf, qf[kk], s[st]);
-        }
-      }
-
-      // logit-scaled scores (-inf where hidden) and the row's tile max
-      const bool masked = t >= n_plain;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[st][r] * c2;
-          if (masked) {
-            const int kj = t * T::BN + 32 * st + acc_row(r, half);
-            bool vis = kj < Sk && qi < Sq;
-            if (CAUSAL) vis = vis && kj <= qi;
-            x = vis ? x : -INFINITY;
-          }
-          s[st][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      }
-      const float mt = pair_max32(mx);
+    // After tile t's max mt (log2 units) is known: the wave-wide test, and the rebase onto
+    // the tile max at most kFp8Bound below the running max.
+    auto update = [&](float mt) {
       m_max = fmaxf(m_max, mt);
-
-      // wave-wide rescale test; rebase onto the tile max, at most kFp8Bound below m_max
       if (__builtin_amdgcn_ballot_w64(mt - m_run > kFp8Tau) != 0) {
         const float m_new = fmaxf(mt, m_max - kFp8Bound);
         const float corr = (m_run == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
@@ -239,42 +228,139 @@ fwd_fp8_kernel(FwdArgs a) {
         for (int db = 0; db < 4; ++db) o[db] *= corr;
         m_run = m_new;
       }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    };
 
-      // exponentials, row sum (unrounded), e4m3 packing: byte 16*st + r of the B operand
-      float rs = 0.f;
+    // Scores of one tile: [st] accumulators, rows = keys 32st + acc_row, column = query.
+    using Scores = f32x16[2];
+
+    // Iteration body as one instruction stream: the four S MFMAs of tile t+1, each with
+    // eight exponentials of tile t, then the four PV MFMAs of tile t, each with eight
+    // elements of tile t+1's row max. Scheduling fences (only scalar instructions may
+    // cross) keep the matrix and vector work of the wave interleaved. MC / MN: tile t /
+    // t+1 needs masking. Returns tile t+1's row max in log2 units.
+    auto body = [&](Scores& nxt, Scores& cur, int t, auto par_tag, auto mc_tag, auto mn_tag) -> float {
+      constexpr int PAR = decltype(par_tag)::value;
+      constexpr bool MC = decltype(mc_tag)::value;
+      constexpr bool MN = decltype(mn_tag)::value;
+      constexpr int KO = (PAR ^ 1) * T::TB;       // K of tile t + 1
+      constexpr int VO = PAR * T::TB;             // V of tile t (vb[] includes V_OFF)
+      const int kc0 = t * T::BN, kn0 = kc0 + T::BN;
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      nxt[0] = f32x16{};
+      nxt[1] = f32x16{};
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+      i32x8 kf = kfrag(KO, 0);
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int i = 0; i < 4; ++i) {
+        i32x8 kn;
+        if (i + 1 < 4) kn = kfrag(KO, i + 1);
+        nxt[i & 1] = mfma32_e4m3(kf, qf[i >> 1], nxt[i & 1]);
+        kf = kn;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(s[st][r] - m_use);
-          s[st][r] = p;
-          rs += p;
+        for (int u = 0; u < 8; ++u) {
+          const int e = 8 * i + u, st = e >> 4, r = e & 15;
+          float pe;
+          if constexpr (!MC) {
+            pe = fast_exp2(fmaf(cur[st][r], c2, -m_use));
+          } else {
+            pe = visible(kc0 + 32 * st + acc_row(r, half)) ? fast_exp2(fmaf(cur[st][r], c2, -m_use)) : 0.f;
+          }
+          cur[st][r] = pe;
+          rs[r & 3] += pe;
+          asm volatile("" : "+v"(rs[r & 3]));   // pin this step's exponential and sum here
         }
+        __builtin_amdgcn_sched_barrier(0x0004);
       }
-      l_run += rs;
+      asm volatile("" : "+v"(rs[0]), "+v"(rs[1]), "+v"(rs[2]), "+v"(rs[3]));
+      l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+      // e4m3 B operand: byte 16*st + r holds the exponential of key 32st + acc_row(r, half)
       i32x8 pf;
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const int st = w >> 2, r = 4 * (w & 3);
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(s[st][r], s[st][r + 1], 0, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(s[st][r + 2], s[st][r + 3], word, true);
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(cur[st][r], cur[st][r + 1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(cur[st][r + 2], cur[st][r + 3], word, true);
         pf[w] = word;
       }
-
-      // O^T += V^T P^T: A bytes 8u..8u+7 from transposed read u (keys 16u + ...)
+      float mx = -INFINITY;
+      i32x8 vf = vfrag(VO, 0);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        i32x2 r0 = lds_read_tr8(vb[db] + kofs + 0 * 16 * T::RB);
-        i32x2 r1 = lds_read_tr8(vb[db] + kofs + 1 * 16 * T::RB);
-        i32x2 r2 = lds_read_tr8(vb[db] + kofs + 2 * 16 * T::RB);
-        i32x2 r3 = lds_read_tr8(vb[db] + kofs + 3 * 16 * T::RB);
-        const i32x8 vf = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+        i32x8 vn;
+        if (db + 1 < 4) vn = vfrag(VO, db + 1);
         o[db] = mfma32_e4m3(vf, pf, o[db]);
+        vf = vn;
+#pragma unroll
+        for (int u = 0; u < 8; u += 2) {
+          const int e0 = 8 * db + u, e1 = e0 + 1;
+          float x0 = nxt[e0 >> 4][e0 & 15], x1 = nxt[e1 >> 4][e1 & 15];
+          if constexpr (MN) {
+            x0 = visible(kn0 + 32 * (e0 >> 4) + acc_row(e0 & 15, half)) ? x0 * c2 : -INFINITY;
+            x1 = visible(kn0 + 32 * (e1 >> 4) + acc_row(e1 & 15, half)) ? x1 * c2 : -INFINITY;
+          }
+          mx = fmaxf(fmaxf(mx, x0), x1);
+          asm volatile("" : "+v"(mx));   // pin this step's part of the max chain here
+        }
+        __builtin_amdgcn_sched_barrier(0x0004);
       }
+      asm volatile("" : "+v"(mx));
+      return MN ? pair_max32(mx) : pair_max32(mx) * c2;
+    };
 
-      wait_vmem();      // this thread's chunks of tile t+1 are in LDS
-      __syncthreads();  // ... everyone's; every wave is done with tile t's buffers
+    // Tile j's K lives in K buffer j & 1 and its V in V buffer j & 1.
+    Scores sa, sb;
+    if (ntiles > 0) {
+      load_k(0, 0);
+      load_v(0, 0);
+    }
+    if (ntiles > 1) load_k(1, 1);
+    wait_vmem();
+    __syncthreads();
+    if (ntiles > 0) {
+      sa[0] = f32x16{};
+      sa[1] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sa[i & 1] = mfma32_e4m3(kfrag(0, i), qf[i >> 1], sa[i & 1]);
+      float mx = -INFINITY;
+      const bool masked = n_plain == 0;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const int st = e >> 4, r = e & 15;
+        const float x = sa[st][r] * c2;
+        mx = fmaxf(mx, (!masked || visible(32 * st + acc_row(r, half))) ? x : -INFINITY);
+      }
+      update(pair_max32(mx));
+    }
+    __syncthreads();  // every wave has read K_0 before K_2 replaces it
+
+    // Iteration t. K buffer PAR (K_t, read by the previous iteration) is refilled with
+    // K_{t+2}; V buffer PAR ^ 1 (V_{t-1}) with V_{t+1}. When t + 1 == ntiles the S MFMAs
+    // read a stale K buffer and their result is discarded.
+    auto iteration = [&](int t, Scores& cur, Scores& nxt, auto par_tag, auto mask_cur, auto mask_nxt) {
+      constexpr int PAR = decltype(par_tag)::value;
+      if (t + 2 < ntiles) load_k(t + 2, PAR);
+      if (t + 1 < ntiles) load_v(t + 1, PAR ^ 1);
+      const float mt = body(nxt, cur, t, par_tag, mask_cur, mask_nxt);
+      if (t + 1 < ntiles) update(mt);
+      wait_vmem();      // this thread's chunks of K_{t+2} and V_{t+1} are in LDS
+      __syncthreads();  // ... everyone's; every wave is done with K_{t+1} and V_t
+    };
+
+    using F = std::integral_constant<bool, false>;
+    using Tr = std::integral_constant<bool, true>;
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    int t = 0;
+    for (; t + 2 < n_plain; t += 2) {
+      iteration(t, sa, sb, P0{}, F{}, F{});
+      iteration(t + 1, sb, sa, P1{}, F{}, F{});
+    }
+    // Remaining tiles in the masked form, still in pairs (the pending scores of the next
+    // tile are in sa at the top of each trip); one form per loop keeps the register
+    // allocation of the two loops apart.
+    for (; t < ntiles; t += 2) {
+      iteration(t, sa, sb, P0{}, Tr{}, Tr{});
+      if (t + 1 < ntiles) iteration(t + 1, sb, sa, P1{}, Tr{}, Tr{});
     }
 
     // Epilogue: out = O * v_descale / l as bf16 rows (through this wave's LDS slice; the
