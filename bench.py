@@ -12,7 +12,11 @@ counted as algorithmic work).
 Prints one JSON line. Per-kernel durations come from HIP events the library records
 around each of its launches on the launch stream during the timed region.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+After the timed steps, and outside them, the fp8 forward (exattn_fwd_fp8, e4m3 inputs with
+per-tensor descales) is timed on the same shape and reported under "fp8_forward" against
+the dense fp8 MFMA peak; it does not enter `value`.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-fp8]
 """
 
 from __future__ import annotations
@@ -29,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd & bwd TFLOP/s (bf16, B2 S8192 H32 D128) + % of MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz (published 2.5 PFLOP/s)
+PEAK_FP8_TFLOPS = 5033.2    # 256 CU x 8192 dense fp8 FLOP/clk x 2.4 GHz (published 5.0 PFLOP/s)
 PEAK_HBM_GBS = 8000.0
 B, S, H, HKV, D = 2, 8192, 32, 32, 128
 PROFILE_DIR = os.path.join(ROOT, "profiles")
@@ -86,12 +91,38 @@ def cpu_baseline(target_seconds=15.0):
                       f"non-causal), forward + backward in float64, {dt:.1f} s"}
 
 
+def fp8_forward(api, workloads, dev, flops, steps, warmup):
+    """Kernel time of exattn_fwd_fp8 on the same shape (e4m3 q, k, v ~ quantised N(0,1))."""
+    import torch
+
+    p = workloads.fp8_dense(B, S, S, H, HKV, D, seed=3002)
+    q, k, v = (t.to(dev) for t in (p.q, p.k, p.v))
+    run = lambda: api.exattn_fwd_fp8(q, k, v, p.q_descale, p.k_descale, p.v_descale)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    api.timing_enable(True)
+    api.timing_read()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    kern = api.timing_read()
+    api.timing_enable(False)
+    t, c = kern["exattn_fwd_fp8_kernel"]
+    ms = t / c
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"kernel": "exattn_fwd_fp8_kernel", "ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+            "peak": PEAK_FP8_TFLOPS, "frac_of_fp8_mfma_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+            "dtype": "e4m3 in, fp32 accumulate, bf16 out"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -198,6 +229,8 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_flops_per_launch": alg},
     }
+    if not args.no_fp8:
+        rec["fp8_forward"] = fp8_forward(api, workloads, dev, fwd_flops, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline()
     print(json.dumps(rec), flush=True)
