@@ -28,6 +28,7 @@ const char* kernel_name(KernelId id) {
     case KernelId::QTail: return "exattn_bwd_q_tail_kernel";
     case KernelId::Zero: return "exattn_zero_kernel";
     case KernelId::FwdFp8: return "exattn_fwd_fp8_kernel";
+    case KernelId::UnitOrder: return "exattn_bwd_unit_order_kernel";
     default: return "unknown";
   }
 }
@@ -192,16 +193,23 @@ Geometry geometry(const exattn_problem* p) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace: [lse2 | Delta] fp32 in the lse layout, then the fp32 dQ accumulator
-// [rows_q, H, D] when the fused variant is selected.
+// Workspace: [lse2 | Delta] fp32 in the lse layout, then (packed layouts) the int32 ranking
+// of the sequences, then the fp32 dQ accumulator [rows_q, H, D] when the fused variant is
+// selected.
 // The fused (atomic) backward is selected by variant 1 and exists for bf16 only.
 bool fused_backward(const exattn_problem* p) {
   return get_bwd_variant() == 1 && p->dtype == EXATTN_DTYPE_BF16;
 }
 
 struct WsLayout {
-  size_t lse2, delta, dq_acc, total;
+  size_t lse2, delta, order, dq_acc, total;
 };
+
+// Packed layouts with at most kMaxOrderedUnits sequences get a ranking of the sequences
+// (int32, longest first) that orders the dK/dV grid.
+bool ordered_units(const exattn_problem* p) {
+  return p->cu_seqlens_q != nullptr && p->num_seqs <= kMaxOrderedUnits;
+}
 
 WsLayout ws_layout(const exattn_problem* p) {
   const Geometry g = geometry(p);
@@ -209,7 +217,8 @@ WsLayout ws_layout(const exattn_problem* p) {
   const size_t nq = (size_t)g.rows_q * p->heads_q;
   w.lse2 = 0;
   w.delta = w.lse2 + align256(nq * sizeof(float));
-  w.dq_acc = w.delta + align256(nq * sizeof(float));
+  w.order = w.delta + align256(nq * sizeof(float));
+  w.dq_acc = w.order + (ordered_units(p) ? align256((size_t)p->num_seqs * sizeof(int32_t)) : 0);
   w.total = w.dq_acc + (fused_backward(p) ? align256(nq * p->head_dim * sizeof(float)) : 0);
   return w;
 }
@@ -421,6 +430,8 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
   a.dq_acc = fused ? reinterpret_cast<float*>(ws + w.dq_acc) : nullptr;
   a.lse2 = reinterpret_cast<float*>(ws + w.lse2);
   a.delta = reinterpret_cast<float*>(ws + w.delta);
+  int32_t* order = ordered_units(p) ? reinterpret_cast<int32_t*>(ws + w.order) : nullptr;
+  a.unit_order = order;
   a.q_sb = p->q_stride[0]; a.q_ss = p->q_stride[1]; a.q_sh = p->q_stride[2];
   a.k_sb = p->k_stride[0]; a.k_ss = p->k_stride[1]; a.k_sh = p->k_stride[2];
   a.v_sb = p->v_stride[0]; a.v_ss = p->v_stride[1]; a.v_sh = p->v_stride[2];
@@ -451,7 +462,7 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
   a.scale = p->scale;
   a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
   a.rotate = fused ? 1 : 0;
-  if ((int64_t)a.num_units * a.Hkv * a.num_k_blocks > INT32_MAX ||
+  if ((((int64_t)a.num_units + 7) / 8 * 8) * a.Hkv * a.num_k_blocks > INT32_MAX ||
       (int64_t)a.num_units * H * a.num_q_blocks > INT32_MAX)
     return fail(EXATTN_ERR_SHAPE, "too many blocks");
 
@@ -463,6 +474,10 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
     if (e == hipSuccess) e = timed(KernelId::Zero, s, [&] { return launch_zero16(dv, bytes, s); });
     if (e != hipSuccess) return hip_fail(e, "zero dk/dv");
     return EXATTN_OK;
+  }
+  if (order) {
+    e = timed(KernelId::UnitOrder, s, [&] { return launch_unit_order(a, order, s); });
+    if (e != hipSuccess) return hip_fail(e, "unit order launch");
   }
   e = timed(KernelId::Delta, s, [&] { return launch_delta(a, D, p->dtype, g.varlen, s); });
   if (e != hipSuccess) return hip_fail(e, "delta kernel launch");

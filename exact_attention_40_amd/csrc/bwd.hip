@@ -1,6 +1,7 @@
 // Backward kernels: recompute P from the stored LSE and produce dQ, dK, dV.
 //
 // Pass order on the caller's stream (default, deterministic variant):
+//   0. unit_order_kernel  packed layouts only: rank the sequences by query length.
 //   1. delta_kernel    Delta_i = sum_d dO_id * O_id (fp32), lse2_i = lse_i * log2(e)
 //                      (+inf for empty rows so exp2(s - lse2) = 0).
 //   2. bwd_kernel      per (unit, kv head, block of 128 keys): dK and dV accumulate in
@@ -156,10 +157,28 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
   // Consecutive blocks are the key blocks of one (unit, kv head): they re-read the same
   // Q/dO tiles, which then stay in one XCD's L2 (also for packed layouts, where ordering
   // by key block across sequences was measured slower).
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  const int kbi = blk % a.num_k_blocks;
-  const int ug = blk / a.num_k_blocks;
-  const int g = ug % a.Hkv, unit = ug / a.Hkv;
+  // Dense: consecutive logical blocks share an XCD (xcd_remap). Packed with a ranking of
+  // the sequences (unit_order: largest q_len * k_len first): the dispatcher sends block b to
+  // XCD b % 8, and XCD x takes the sequences of rank 8s + x (s even) or 8s + 7 - x (s odd),
+  // a snake deal that gives every XCD a similar share of the work; each sequence's blocks
+  // stay on one XCD (its Q/dO re-reads hit that XCD's L2), largest sequences first.
+  int kbi, g, unit;
+  if (VARLEN && a.unit_order) {
+    const int per_unit = a.Hkv * a.num_k_blocks;
+    const int x = (int)(blockIdx.x & 7), k = (int)(blockIdx.x >> 3);
+    const int slot = k / per_unit, within = k - slot * per_unit;
+    const int r = 8 * slot + ((slot & 1) ? 7 - x : x);
+    if (r >= a.num_units) return;
+    unit = a.unit_order[r];
+    g = within / a.num_k_blocks;
+    kbi = within - g * a.num_k_blocks;
+  } else {
+    const int blk = xcd_remap(blockIdx.x, gridDim.x);
+    kbi = blk % a.num_k_blocks;
+    const int ug = blk / a.num_k_blocks;
+    g = ug % a.Hkv;
+    unit = ug / a.Hkv;
+  }
 
   int Sq, Sk;
   int64_t qrow0, krow0, qb_off, kb_off, vb_off, dob_off, st_unit;
@@ -535,9 +554,9 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31, grp = lane >> 4, j16 = lane & 15;
 
-  // Block order as in the forward: packed layouts take the query-tile index outermost.
-  // Dense causal: tiles n-1-j and j in one workgroup (equal work per block).
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  // Block order as in the forward: packed layouts take the query-tile index outermost
+  // (and no XCD remap). Dense causal: tiles n-1-j and j in one workgroup (equal work).
+  const int blk = VARLEN ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
   const int n_qtiles = a.num_q_blocks;
   int qtile, qtile2 = -1, uh;
   if constexpr (VARLEN) {
@@ -804,6 +823,21 @@ __global__ void __launch_bounds__(256) q_tail_kernel(BwdArgs a, int64_t row_chun
   reinterpret_cast<u32x4*>(a.dq)[i] = u32x4{0, 0, 0, 0};
 }
 
+// Packed layouts: order[rank] = sequence, ranked by q_len * k_len (largest first, ties by
+// index). The ranks form a permutation, so every slot is written exactly once.
+__global__ void __launch_bounds__(256) unit_order_kernel(const int32_t* cu_q, const int32_t* cu_k,
+                                                         int n, int32_t* order) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int64_t wi = (int64_t)(cu_q[i + 1] - cu_q[i]) * (cu_k[i + 1] - cu_k[i]);
+  int rank = 0;
+  for (int j = 0; j < n; ++j) {
+    const int64_t wj = (int64_t)(cu_q[j + 1] - cu_q[j]) * (cu_k[j + 1] - cu_k[j]);
+    rank += (wj > wi) || (wj == wi && j < i);
+  }
+  order[rank] = i;
+}
+
 // Zero-fill of a buffer, 16 bytes per thread (used instead of a memset node so that the
 // call stays capturable into a graph).
 __global__ void __launch_bounds__(256) zero16_kernel(u32x4* p, int64_t n16) {
@@ -819,6 +853,14 @@ hipError_t launch_zero16(void* p, int64_t bytes, hipStream_t s) {
   if (n16 <= 0) return hipSuccess;
   dim3 grid((unsigned)((n16 + 255) / 256)), block(256);
   hipLaunchKernelGGL(zero16_kernel, grid, block, 0, s, reinterpret_cast<u32x4*>(p), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_unit_order(const BwdArgs& a, int32_t* order, hipStream_t s) {
+  const int n = a.num_units;
+  if (n <= 0) return hipSuccess;
+  dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  hipLaunchKernelGGL(unit_order_kernel, grid, block, 0, s, a.cu_q, a.cu_k, n, order);
   return hipGetLastError();
 }
 
@@ -855,7 +897,9 @@ hipError_t launch_delta(const BwdArgs& a, int head_dim, int dtype, bool varlen, 
 // split backward.
 template <class E, int D, bool FUSED>
 static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, int mask, bool varlen, hipStream_t s) {
-  const int64_t nblk = (int64_t)a.num_units * a.Hkv * a.num_k_blocks;
+  // with a sequence ranking (packed): 8 XCDs x ceil(units / 8) slots of whole sequences
+  const int64_t units = (varlen && a.unit_order) ? 8 * (((int64_t)a.num_units + 7) / 8) : a.num_units;
+  const int64_t nblk = units * a.Hkv * a.num_k_blocks;
   if (nblk <= 0) return hipSuccess;
   dim3 grid((unsigned)nblk), block(512);
   constexpr int smem = (int)bwd_smem_bytes<D, FUSED>();

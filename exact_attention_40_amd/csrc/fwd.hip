@@ -77,11 +77,13 @@ fwd_kernel(FwdArgs a) {
 
   // Dense: consecutive blocks are the query tiles of one (unit, head), which share K/V in
   // one XCD's L2. Packed: query-tile index outermost, highest first, so that the longest
-  // blocks of every sequence (whatever its length) start before the short ones.
+  // blocks of every sequence (whatever its length) start before the short ones; without
+  // the XCD remap, so that each tile layer (heavy high layers, light low ones) is spread
+  // over all XCDs instead of one XCD taking the heavy layers.
   // Dense causal: block j of a (unit, head) runs query tiles n-1-j and j one after the
   // other (tile i sees i+1 key tiles), so every block has the same amount of work and no
   // long tile is left for the end of the grid.
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int blk = VARLEN ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
   int qtile, qtile2 = -1, uh;
   if constexpr (VARLEN) {
     const int nuh = a.num_units * a.H;

@@ -41,6 +41,7 @@ struct BwdArgs {
   float* dq_acc;     // fp32 [rows_q, H, D], fused variant only (else NULL)
   float* lse2;       // fp32, lse layout: lse * log2(e), +inf for empty rows
   float* delta;      // fp32, lse layout: rowsum(dout * out)
+  const int32_t* unit_order;  // packed: sequences by query length, longest first (NULL = in order)
   int64_t q_sb, q_ss, q_sh;
   int64_t k_sb, k_ss, k_sh;
   int64_t v_sb, v_ss, v_sh;
@@ -63,7 +64,8 @@ struct BwdArgs {
 };
 
 enum class KernelId : int {
-  Fwd = 0, FwdTail, Delta, BwdDkDv, BwdDq, BwdFused, DqReduce, KvTail, QTail, Zero, FwdFp8, Count
+  Fwd = 0, FwdTail, Delta, BwdDkDv, BwdDq, BwdFused, DqReduce, KvTail, QTail, Zero, FwdFp8,
+  UnitOrder, Count
 };
 
 const char* kernel_name(KernelId id);
@@ -81,6 +83,8 @@ hipError_t launch_q_tail(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_dq_reduce(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_kv_tail(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_zero16(void* p, int64_t bytes, hipStream_t s);  // bytes % 16 == 0
+constexpr int kMaxOrderedUnits = 8192;  // packed sequences ranked for the dK/dV grid, at most
+hipError_t launch_unit_order(const BwdArgs& a, int32_t* order, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdArgs& a, bool causal, hipStream_t s);  // head_dim 128, dense
 
 // Tile shapes the host needs for grid sizing, and the tiling selectors.

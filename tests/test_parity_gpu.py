@@ -197,6 +197,19 @@ def test_varlen_thd_shapes(lengths):
     _check_varlen(p, g, [(s, h) for s in range(len(lengths)) for h in range(2)])
 
 
+def test_varlen_many_sequences_with_ties_and_empties():
+    """300 packed sequences (more than one 256-thread block of the ranking pass) with many
+    equal lengths and some empty ones: the dK/dV grid walks them longest first, and every
+    sequence must still be computed exactly once."""
+    rng = np.random.default_rng(4300)
+    lengths = rng.choice([0, 1, 17, 64, 64, 128, 129, 200], size=300).tolist()
+    p = workloads.varlen_gqa(seed=4301, lengths=lengths, H=2, Hkv=1)
+    g = run_gpu(p)
+    for n in ("out", "dq", "dk", "dv"):
+        assert nonfinite(g[n]) == 0, n
+    _check_varlen(p, g, [(s, 0) for s in range(300) if lengths[s] > 0])
+
+
 def test_long_causal_sampled():
     """B1 S61380 H32 D128 causal: 64 sampled query rows (out, lse, dq), sampled keys near
     the end (dk, dv), the gradient sums over all keys, zero non-finite values."""
