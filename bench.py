@@ -91,6 +91,29 @@ def cpu_baseline(target_seconds=15.0):
                       f"non-causal), forward + backward in float64, {dt:.1f} s"}
 
 
+def device_info(dev):
+    """CU count and top shader clock as read on this machine, next to the nominal values
+    the peaks use (256 CUs, 2.4 GHz). The clock comes from the amdgpu driver's DPM table in
+    sysfs (the highest listed level); null when it cannot be read."""
+    import glob
+    import re
+
+    import torch
+
+    props = torch.cuda.get_device_properties(dev)
+    mhz = None
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            levels = [int(m) for m in re.findall(r"(\d+)\s*Mhz", open(path).read(), flags=re.I)]
+        except OSError:
+            continue
+        if levels:
+            mhz = max(mhz or 0, max(levels))
+    return {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+            "cus": props.multi_processor_count, "max_sclk_mhz": mhz,
+            "nominal": {"cus": 256, "sclk_mhz": 2400}}
+
+
 def fp8_forward(api, workloads, dev, flops, steps, warmup):
     """Kernel time of exattn_fwd_fp8 on the same shape (e4m3 q, k, v ~ quantised N(0,1))."""
     import torch
@@ -221,6 +244,7 @@ def main():
                 "frac_of_mfma_peak": round(fwd_flops / fwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4)},
         "bwd": {"ms": round(bwd_ms, 4), "TFLOP/s": round(bwd_flops / bwd_ms / 1e9, 1),
                 "frac_of_mfma_peak": round(bwd_flops / bwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4)},
+        "device": device_info(dev),
         "kernels_avg_ms": {n: round(t, 4) for n, t in kavg.items()},
         "kernels": kernels,
         "side_passes": side,

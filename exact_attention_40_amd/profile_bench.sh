@@ -8,10 +8,11 @@ R=${GRAFT_REPO_ROOT:-$(cd "$(dirname "$0")/.." && pwd)}
 O=$R/gpurun_out/prof
 mkdir -p $O
 cd $R
-echo "trace" && timeout -k 10 240 rocprofv3 --kernel-trace --stats -d $O/trace -o bench -f csv -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline > $O/trace.log 2>&1 || exit 1
+echo "trace" && timeout -k 10 240 rocprofv3 --kernel-trace --stats -d $O/trace -o bench -f csv -- python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline > $O/trace.log 2>&1 || exit 1
 echo "fetch" && timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d $O/fetch -o bench -f csv -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline > $O/fetch.log 2>&1 || exit 1
 echo "write" && timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d $O/write -o bench -f csv -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline > $O/write.log 2>&1 || exit 1
 echo "copy fetch" && timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d $O/cfetch -o copy -f csv -- python3 -m exact_attention_40_amd.copy_probe 512 > $O/cfetch.log 2>&1 || exit 1
 echo "copy write" && timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d $O/cwrite -o copy -f csv -- python3 -m exact_attention_40_amd.copy_probe 512 > $O/cwrite.log 2>&1 || exit 1
 python3 -m exact_attention_40_amd.traffic $(ls $O/fetch/*counter_collection.csv) $(ls $O/write/*counter_collection.csv) $(ls $O/cfetch/*counter_collection.csv) $(ls $O/cwrite/*counter_collection.csv) 512 $O
-# the per-kernel JSON files land in gpurun_out/prof; copy them into profiles/ to commit them
+python3 -m exact_attention_40_amd.profile_summary $O $O/exattn_b2_s8192_h32_d128_kernel_stats.md 20
+# the per-kernel JSON files and the summary land in gpurun_out/prof; copy them into profiles/

@@ -1,7 +1,7 @@
 """Writes the kernel-duration and HBM-traffic summary for profiles/ from the output of
 profile_bench.sh (rocprofv3 kernel stats CSV and the per-kernel traffic JSON files).
 
-    python -m exact_attention_40_amd.profile_summary PROF_DIR OUT.md
+    python -m exact_attention_40_amd.profile_summary PROF_DIR OUT.md [TIMED_STEPS]
 """
 
 import csv
@@ -17,6 +17,7 @@ MIN_BYTES = {  # algorithmic bytes per launch at B=2 S=8192 H=32 D=128 (bf16 ten
     "exattn_bwd_dkdv_kernel": ("q, k, v, dout 0.537 GB + lse2, delta 0.004 GB read; dk, dv 0.268 GB written", 0.5411, 0.2684),
     "exattn_bwd_dq_kernel": ("q, k, v, dout 0.537 GB + stats 0.004 GB read; dq 0.134 GB written", 0.5411, 0.1342),
     "exattn_bwd_delta_kernel": ("out, dout 0.268 GB + lse read; delta, lse2 0.004 GB written", 0.2705, 0.0042),
+    "exattn_fwd_fp8_kernel": ("e4m3 q, k, v read 0.201 GB; bf16 out + lse written 0.136 GB", 0.2013, 0.1363),
 }
 
 
@@ -27,27 +28,46 @@ def short(name):
     return name
 
 
+def timed_averages(prof, steps):
+    """Average duration (ms) of each kernel over its last `steps` dispatches: the calls of
+    the benchmark's timed steps (the trace also holds the warm-up calls)."""
+    durs = {}
+    for r in csv.DictReader(open(os.path.join(prof, "trace", "bench_kernel_trace.csv"))):
+        durs.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    out = {}
+    for name, d in durs.items():
+        last = [x for _, x in sorted(d)][-steps:]
+        out[name] = sum(last) / len(last) / 1e6
+    return out
+
+
 def main():
     prof, out = sys.argv[1:3]
+    steps = int(sys.argv[3]) if len(sys.argv) > 3 else 20
     rows = list(csv.DictReader(open(os.path.join(prof, "trace", "bench_kernel_stats.csv"))))
+    timed = timed_averages(prof, steps)
     lines = [
         "# Kernel durations and HBM traffic: fwd + bwd step, B=2 S=8192 H=32 Hkv=32 D=128 (non-causal, bf16)",
         "",
-        "Kernel trace (rocprofv3 `--kernel-trace --stats`) over 2 warm-up and 5 timed bench steps, so the",
-        "average includes the first (cold) calls; the minimum is the steady state that bench.py's",
-        "in-process HIP-event timing sees.",
+        "Kernel trace (rocprofv3 `--kernel-trace --stats`) over the benchmark's warm-up and timed steps.",
+        f"\"timed avg\" is the mean over each kernel's last {steps} dispatches (the timed steps, from the",
+        "per-dispatch trace); it is the figure to compare with bench.py's in-process HIP-event timing.",
+        "\"avg\" includes the first (cold) calls.",
         "",
         "Command (from the repository root; `exact_attention_40_amd/profile_bench.sh` runs all passes):",
         "",
         "```",
-        "rocprofv3 --kernel-trace --stats -d gpurun_out/prof/trace -o bench -f csv -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+        f"rocprofv3 --kernel-trace --stats -d gpurun_out/prof/trace -o bench -f csv -- python3 bench.py --steps {steps} --warmup 5 --no-cpu-baseline",
         "```",
         "",
-        "| kernel | instance | calls | avg ms | min ms | max ms | share |",
-        "|---|---|---|---|---|---|---|",
+        "| kernel | instance | calls | timed avg ms | avg ms | min ms | max ms | share |",
+        "|---|---|---|---|---|---|---|---|",
     ]
     for r in rows:
-        lines.append(f"| {short(r['Name'])} | `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
+        t = timed.get(r["Name"])
+        lines.append(f"| {short(r['Name'])} | `{r['Name']}` | {r['Calls']} | "
+                     f"{'' if t is None else f'{t:.3f}'} | {float(r['AverageNs']) / 1e6:.3f} | "
                      f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} | {float(r['Percentage']):.1f}% |")
     lines += [
         "",

@@ -22,6 +22,7 @@ KERNELS = {  # library timing name -> kernel template name (rocprofv3 may or may
     "exattn_bwd_dkdv_kernel": "bwd_kernel",
     "exattn_bwd_dq_kernel": "bwd_dq_kernel",
     "exattn_bwd_delta_kernel": "delta_kernel",
+    "exattn_fwd_fp8_kernel": "fwd_fp8_kernel",
 }
 
 
@@ -72,7 +73,8 @@ def main():
             continue
         rec = {
             "kernel": name,
-            "workload": "B=2 S=8192 H=32 Hkv=32 D=128 non-causal bf16",
+            "workload": "B=2 S=8192 H=32 Hkv=32 D=128 non-causal "
+                        + ("e4m3" if name == "exattn_fwd_fp8_kernel" else "bf16"),
             "fetch_bytes_per_launch": sum(fk) / len(fk) * 1024 * fscale,
             "write_bytes_per_launch": sum(wk) / len(wk) * 1024 * wscale,
             "copy_calibration": {"bytes": copy_bytes, "fetch_factor": fscale, "write_factor": wscale},
