@@ -30,6 +30,10 @@
 
 namespace exattn {
 
+// min(x, 0) that keeps NaN (v_minimum3_f32): the exponent clamp must not turn a NaN score
+// or lse into exp2(0) = 1.
+__device__ __forceinline__ float min0(float x) { return __builtin_elementwise_minimum(x, 0.f); }
+
 template <bool B>
 using bool_c = std::integral_constant<bool, B>;
 
@@ -357,7 +361,7 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rg + e;
           if constexpr (!EDGE) {
-            s[r] = fast_exp2(fminf(fmaf(s[r], c2, -l2[e]), 0.f));
+            s[r] = fast_exp2(min0(fmaf(s[r], c2, -l2[e])));
           } else {
             // Branch-free visibility: mask reads use indices clamped into range.
             const int qi = qt0 + qb * 32 + 8 * rg + 4 * half + e;
@@ -374,7 +378,7 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
                 b2 = vis ? bias * kLog2e : 0.f;
               }
             }
-            const float e2 = fast_exp2(fminf(fmaf(s[r], c2, b2 - l2[e]), 0.f));
+            const float e2 = fast_exp2(min0(fmaf(s[r], c2, b2 - l2[e])));
             s[r] = vis ? e2 : 0.f;
           }
         }
@@ -704,7 +708,7 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
       for (int r = 0; r < 16; ++r) {
         float p;
         if constexpr (!MASKED) {
-          p = fast_exp2(fminf(fmaf(s[kb][r], c2, -l2), 0.f));
+          p = fast_exp2(min0(fmaf(s[kb][r], c2, -l2)));
         } else {
           const int kj = kb0 + kb * 32 + acc_row(r, half);
           bool vis = (kj < Sk) && (qi < Sq);
@@ -720,7 +724,7 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
               b2 = vis ? bias * kLog2e : 0.f;
             }
           }
-          const float e2 = fast_exp2(fminf(fmaf(s[kb][r], c2, b2 - l2), 0.f));
+          const float e2 = fast_exp2(min0(fmaf(s[kb][r], c2, b2 - l2)));
           p = vis ? e2 : 0.f;
         }
         dp[kb][r] = p * (dp[kb][r] - dl);

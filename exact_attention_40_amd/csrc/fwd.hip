@@ -475,7 +475,7 @@ fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l = l_run[qb] + wave_xor32(l_run[qb]);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float inv = l != 0.f ? 1.f / l : 0.f;   // NaN propagates
     const int r0 = qt0 + (wave * QB + qb) * 32;
     E* orow = reinterpret_cast<E*>(a.out) + o_base + (int64_t)r0 * a.o_ss;
     static_assert(NW * QB * 32 * D * 2 <= 4 * T::TBYTES, "epilogue staging fits the tile buffers");
@@ -483,7 +483,7 @@ fwd_kernel(FwdArgs a) {
                        Sq - r0, lane);
     if (qi[qb] < Sq && half == 0) {
       const float mu = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-      a.lse[lse_base + qi[qb]] = l > 0.f ? (mu + log2f(l)) * kLn2 : -INFINITY;
+      a.lse[lse_base + qi[qb]] = l != 0.f ? (mu + log2f(l)) * kLn2 : -INFINITY;
     }
   }
   };

@@ -366,13 +366,13 @@ fwd_fp8_kernel(FwdArgs a) {
     // Epilogue: out = O * v_descale / l as bf16 rows (through this wave's LDS slice; the
     // tile buffers are free after the last barrier), lse in natural-log units.
     const float l = l_run + wave_xor32(l_run);
-    const float inv = l > 0.f ? a.v_descale / l : 0.f;
+    const float inv = l != 0.f ? a.v_descale / l : 0.f;   // NaN propagates
     const int r0 = qt0 + wave * 32;
     bf16* orow = reinterpret_cast<bf16*>(a.out) + o_base + (int64_t)r0 * a.o_ss;
     wave_store_rows<T::D, bf16>(smem + wave * 32 * T::D * 2, o, inv, orow, a.o_ss, Sq - r0, lane);
     if (qi < Sq && half == 0) {
       const float mu = (m_run == -INFINITY) ? 0.f : m_run;
-      a.lse[lse_base + qi] = l > 0.f ? (mu + log2f(l)) * kLn2 : -INFINITY;
+      a.lse[lse_base + qi] = l != 0.f ? (mu + log2f(l)) * kLn2 : -INFINITY;
     }
   };
 

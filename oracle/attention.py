@@ -96,7 +96,7 @@ def unit_forward(q, k, v, scale, vis, bias=None):
     s = _scores(q, k, scale, bias)
     s_vis = np.where(vis, s, -np.inf)
     m = s_vis.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
-    nonempty = np.isfinite(m)
+    nonempty = vis.any(axis=1) if s.shape[1] else np.zeros(s.shape[0], dtype=bool)
     m_safe = np.where(nonempty, m, 0.0)
     e = np.where(vis, np.exp(s_vis - m_safe[:, None]), 0.0)
     l = e.sum(axis=1)

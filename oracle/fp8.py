@@ -149,7 +149,7 @@ def fp8_forward(q8, k8, v8, q_descale, k_descale, v_descale, *, causal=False, sc
             with np.errstate(over="ignore", invalid="ignore"):
                 acc = acc + pq @ v8[b, cols, g, :]
         m_use = np.where(m == -np.inf, 0.0, m)
-        ok = l > 0
+        ok = l != 0                    # NaN sums propagate
         with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
             out[b, rows, h, :] = np.where(ok[:, None], acc * v_descale / np.where(ok, l, 1.0)[:, None], 0.0)
             lse[b, h, rows] = np.where(ok, (m_use + np.log2(np.where(ok, l, 1.0))) * _LN2, -np.inf)

@@ -142,3 +142,30 @@ def test_fp8_full_size_sampled():
     e_lse = rel_l2(gl[~np.isnan(rl)], rl[~np.isnan(rl)])
     say(f"[fp8 full size sampled] out rel-L2 {e_out:.3e}  lse rel-L2 {e_lse:.3e}")
     assert e_out <= TOL_NORMAL["out"] and e_lse <= TOL_NORMAL["lse"]
+
+
+def test_fp8_nan_input_propagates():
+    """An e4m3 NaN in one query row: that row's out and lse are NaN, the other rows equal
+    the clean run bit for bit."""
+    p = workloads.fp8_dense(1, 300, 260, 2, 1, 128, seed=9500)
+    o0, l0 = _run(p)
+    q = p.q.clone()
+    q.view(torch.uint8)[0, 77, 1, 5] = 0x7F                 # e4m3 NaN
+    o1, l1 = api.exattn_fwd_fp8(q.cuda(), p.k.cuda(), p.v.cuda(), p.q_descale, p.k_descale,
+                                p.v_descale)
+    torch.cuda.synchronize()
+    assert torch.isnan(o1[0, 77, 1]).all() and torch.isnan(l1[0, 1, 77])
+    keep = torch.ones(o1.shape[:3], dtype=torch.bool, device="cuda")
+    keep[0, 77, 1] = False
+    assert torch.equal(o1[keep], o0[keep])
+
+
+@pytest.mark.parametrize("k_mult", [1000.0, 5000.0, 20000.0])
+def test_fp8_page_wide_range_value_ones(k_mult):
+    """FlyDSL PR #1033, "The fp8 helper, second commit": V = ones with K scaled by 1000 to
+    20000 stays finite with a bound of 16 (the uncapped rebase gave NaN there); out stays
+    within the e4m3 rounding of 1 and lse matches the oracle."""
+    p = workloads.fp8_dense(1, 512, 4096, 2, 1, 128, seed=9600, k_mult=k_mult, v_ones=True)
+    go, gl, ro, _ = _check(p, TOL_NORMAL, f"wide_v_ones_k{k_mult:g}")
+    assert np.isfinite(gl).all()
+    assert np.mean(np.abs(go - 1.0)) < 5e-3

@@ -13,7 +13,9 @@
 * With V = ones the output stays near 1 (the section's V = ones measurements).
 """
 
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -22,6 +24,8 @@ import torch
 import oracle
 from oracle.fp8 import fp8_forward, round_e4m3
 from exact_attention_40_amd import workloads
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_values.json")))
 
 
 def _rel(a, b):
@@ -190,3 +194,22 @@ def test_cap_bounds_the_base_below_the_running_max():
     assert st["triggers"] == ntile and st["lowered"] == 1
     assert np.allclose(out, 1.0, rtol=0, atol=1e-12)
     assert abs(lse[0, 0, 1] - math.log(n)) < 1e-9
+
+
+def test_page_fp8_table_wide_range_v_ones():
+    """FlyDSL PR #1033, "The fp8 helper, second commit" (tests/golden/page_values.json,
+    fp8_bound_table): with V = ones and K scaled by 5000 or 20000 the uncapped rebase
+    produced NaN while a bound of 16 kept every output finite with mean |o - 1| at most a
+    few 1e-3. The same holds for the oracle (on fewer keys than the page's 12288)."""
+    g = GOLDEN["fp8_bound_table"]
+    worst = max(x for x in g["bound_16_mean_abs_o_minus_1"] if x is not None)
+    for km in g["k_scale"]:
+        p = workloads.fp8_dense(1, 64, 2048, 2, 1, 32, seed=37, k_mult=float(km), v_ones=True)
+        q, k, v = p.decoded()
+        out, _ = fp8_forward(q, k, v, p.q_descale, p.k_descale, p.v_descale)
+        assert np.all(np.isfinite(out))
+        assert np.mean(np.abs(out - 1.0)) <= 5 * worst
+        if km >= 5000:
+            with np.errstate(all="ignore"):
+                free, _ = fp8_forward(q, k, v, p.q_descale, p.k_descale, p.v_descale, bound=None)
+            assert not np.all(np.isfinite(free))

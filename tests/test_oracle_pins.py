@@ -488,3 +488,28 @@ def test_anti_aligned_row_lse_matches_page(shape, kind):
         # below the point where exp(0 - lse) overflows fp32
         assert np.all(row < GOLDEN["exp_overflow_lse"]["value"])
     assert np.isfinite(out).all()
+
+
+def test_nonfinite_inputs_propagate():
+    """Reading: non-finite inputs propagate through IEEE arithmetic and are never cleaned.
+    A NaN in one query row makes that row's out, lse and dq NaN and, since the row sees
+    every key, all of dk and dv; the other rows' out, lse and dq are unchanged bit for
+    bit. A NaN in one key reaches every row that sees it."""
+    rng = np.random.default_rng(77)
+    q, k, v, do = (rng.standard_normal(s) for s in ((1, 6, 2, 8), (1, 5, 1, 8), (1, 5, 1, 8), (1, 6, 2, 8)))
+    o0, l0 = oracle.attention_forward(q, k, v)
+    g0 = oracle.attention_backward(q, k, v, do)
+    qn = q.copy()
+    qn[0, 2, 1, 3] = np.nan
+    o1, l1 = oracle.attention_forward(qn, k, v)
+    dq1, dk1, dv1 = oracle.attention_backward(qn, k, v, do)
+    assert np.all(np.isnan(o1[0, 2, 1])) and np.isnan(l1[0, 1, 2]) and np.all(np.isnan(dq1[0, 2, 1]))
+    keep = np.ones(o1.shape[:3], dtype=bool)
+    keep[0, 2, 1] = False
+    assert np.array_equal(o1[keep], o0[keep]) and np.array_equal(dq1[keep], g0[0][keep])
+    assert np.array_equal(np.delete(l1[0, 1], 2), np.delete(l0[0, 1], 2)) and np.array_equal(l1[0, 0], l0[0, 0])
+    assert np.all(np.isnan(dk1)) and np.all(np.isnan(dv1))
+    kn = k.copy()
+    kn[0, 4, 0, 0] = np.nan
+    o2, _ = oracle.attention_forward(q, kn, v, causal=True)
+    assert np.all(np.isfinite(o2[0, :4])) and np.all(np.isnan(o2[0, 4:]))   # rows >= 4 see key 4

@@ -168,3 +168,27 @@ def test_rejects_cpu_and_mixed_devices():
     with pytest.raises(ValueError):
         api.exattn_fwd(qg, kg, vg, mask=torch.ones(64, 64, dtype=torch.bool))
     say("contract checks ok")
+
+
+def test_nan_input_propagates_and_stays_local():
+    """A NaN in one query row (reading: non-finite inputs propagate, never cleaned): that
+    row's out, lse and dq are NaN, every other row's out, lse and dq equal the clean run bit
+    for bit, and dk / dv of the KV head the row reads are NaN (the row sees every key). The
+    exponent clamp of the backward keeps the NaN (a plain min would turn it into exp2(0))."""
+    p = workloads.dense(1, 300, 260, 2, 1, 128, seed=6100)
+    q, k, v, do = (t.cuda() for t in (p.q, p.k, p.v, p.dout))
+    o0, l0 = api.exattn_fwd(q, k, v)
+    g0 = api.exattn_bwd(q, k, v, o0, do, l0)
+    qn = q.clone()
+    qn[0, 77, 1, 5] = float("nan")
+    o1, l1 = api.exattn_fwd(qn, k, v)
+    dq1, dk1, dv1 = api.exattn_bwd(qn, k, v, o1, do, l1)
+    torch.cuda.synchronize()
+    assert torch.isnan(o1[0, 77, 1]).all() and torch.isnan(l1[0, 1, 77]) and torch.isnan(dq1[0, 77, 1]).all()
+    keep = torch.ones(o1.shape[:3], dtype=torch.bool, device="cuda")
+    keep[0, 77, 1] = False
+    assert torch.equal(o1[keep], o0[keep]) and torch.equal(dq1[keep], g0[0][keep])
+    lk = torch.ones_like(l1, dtype=torch.bool)
+    lk[0, 1, 77] = False
+    assert torch.equal(l1[lk], l0[lk])
+    assert torch.isnan(dk1).all() and torch.isnan(dv1).all()
