@@ -765,15 +765,26 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
     tile(t, std::integral_constant<int, 0>{}, bool_c<false>{});
     tile(t + 1, std::integral_constant<int, 1>{}, bool_c<false>{});
   }
-  // Remaining tiles (odd plain tile, masked tiles) with a run-time buffer parity.
-  for (; t < ntiles; ++t) {
-    const bool plain = t < n_plain;
-    if ((t & 1) == 0) {
-      if (plain) tile(t, std::integral_constant<int, 0>{}, bool_c<false>{});
-      else tile(t, std::integral_constant<int, 0>{}, bool_c<true>{});
-    } else {
-      if (plain) tile(t, std::integral_constant<int, 1>{}, bool_c<false>{});
-      else tile(t, std::integral_constant<int, 1>{}, bool_c<true>{});
+  if constexpr (CAUSAL || MASK != kMaskNone || VARLEN) {
+    // Remaining tiles (at most one unmasked, then the masked ones) in the masked form, in
+    // pairs of fixed buffer parity: one form per loop keeps the register allocation of the
+    // two loops apart (a run-time choice between forms inside one loop spills).
+    for (; t < ntiles; t += 2) {
+      tile(t, std::integral_constant<int, 0>{}, bool_c<true>{});
+      if (t + 1 < ntiles) tile(t + 1, std::integral_constant<int, 1>{}, bool_c<true>{});
+    }
+  } else {
+    // Dense, unmasked, non-causal: only an odd last tile and a partial key tile remain.
+    // This form measured about 1% faster for the main loop above than the paired one.
+    for (; t < ntiles; ++t) {
+      const bool plain = t < n_plain;
+      if ((t & 1) == 0) {
+        if (plain) tile(t, std::integral_constant<int, 0>{}, bool_c<false>{});
+        else tile(t, std::integral_constant<int, 0>{}, bool_c<true>{});
+      } else {
+        if (plain) tile(t, std::integral_constant<int, 1>{}, bool_c<false>{});
+        else tile(t, std::integral_constant<int, 1>{}, bool_c<true>{});
+      }
     }
   }
 
