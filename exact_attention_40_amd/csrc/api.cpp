@@ -483,8 +483,10 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
   if (e != hipSuccess) return hip_fail(e, "delta kernel launch");
   const bool causal = p->causal != 0;
   if (a.num_k_blocks > 0) {
+    const bool pipelined = !fused && get_bwd_variant() != 2;
     e = timed(fused ? KernelId::BwdFused : KernelId::BwdDkDv, s, [&] {
-      return launch_bwd(a, D, p->dtype, causal, p->mask_kind, g.varlen, fused, s);
+      return pipelined ? launch_bwd_kv(a, D, p->dtype, causal, p->mask_kind, g.varlen, s)
+                       : launch_bwd(a, D, p->dtype, causal, p->mask_kind, g.varlen, fused, s);
     });
     if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
   }
@@ -512,7 +514,7 @@ exattn_status exattn_set_variant(int kernel, int variant) {
     set_fwd_variant(variant);
     return EXATTN_OK;
   }
-  if (kernel == 1 && (variant == 0 || variant == 1)) {
+  if (kernel == 1 && variant >= 0 && variant <= 2) {
     set_bwd_variant(variant);
     return EXATTN_OK;
   }

@@ -30,13 +30,6 @@
 
 namespace exattn {
 
-// min(x, 0) that keeps NaN (v_minimum3_f32): the exponent clamp must not turn a NaN score
-// or lse into exp2(0) = 1.
-__device__ __forceinline__ float min0(float x) { return __builtin_elementwise_minimum(x, 0.f); }
-
-template <bool B>
-using bool_c = std::integral_constant<bool, B>;
-
 // ----------------------------------------------------------------------------------------
 // 1. Delta / lse2 / dQ-accumulator clear. One group of D/8 lanes per (row, head).
 // ----------------------------------------------------------------------------------------
@@ -638,6 +631,8 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
     n_plain = min(lim, ntiles);
   }
 
+  // K/V tiles go straight into LDS through the compiler's direct-to-LDS loads. (The
+  // asynchronous copies the forward and dK/dV kernels use measured about 1% slower here.)
   auto load_tile = [&](int t, int buf) {
     const int kb0 = t * T::BN;
     const int rows = min(T::BN, Sk - kb0);
@@ -881,10 +876,11 @@ hipError_t launch_unit_order(const BwdArgs& a, int32_t* order, hipStream_t s) {
 
 int bwd_block_n(int head_dim) { return BwdTile<128>::BN; }
 
-// Backward variants: 0 = dK/dV kernel + separate dQ kernel (deterministic), 1 = one fused
-// kernel with fp32 dQ atomics.
+// Backward variants: 0 = pipelined dK/dV kernel (bwd_kv.hip) + separate dQ kernel
+// (deterministic), 1 = one fused kernel with fp32 dQ atomics, 2 = the two-barrier dK/dV
+// kernel above + the same dQ kernel.
 static int g_bwd_variant = 0;
-void set_bwd_variant(int v) { g_bwd_variant = (v == 1) ? 1 : 0; }
+void set_bwd_variant(int v) { g_bwd_variant = (v == 1 || v == 2) ? v : 0; }
 int get_bwd_variant() { return g_bwd_variant; }
 
 template <class E>

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace exattn {
 
 typedef __bf16 bf16;
@@ -53,6 +55,13 @@ struct Ty<f16> {
 __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// min(x, 0) that keeps NaN (v_minimum3_f32): the backward's exponent clamp must not turn a
+// NaN score or lse into exp2(0) = 1.
+__device__ __forceinline__ float min0(float x) { return __builtin_elementwise_minimum(x, 0.f); }
+
+template <bool B>
+using bool_c = std::integral_constant<bool, B>;
 
 // Eight fp32 values rounded (to nearest even) to one 16-byte fragment of the input format.
 template <class V8 = bf16x8>
@@ -147,6 +156,51 @@ __device__ __forceinline__ void copy_tile_to_lds(unsigned char* dst, __amdgpu_bu
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Asynchronous global -> LDS copies (buffer loads with the LDS bit): lane i writes its
+// 16 (or 4) bytes at LDS byte address `lds` + 16*i (or + 4*i); reads past `bytes` of the
+// buffer return zero. They are issued from inline assembly so that the compiler does not
+// treat them as LDS writes that every later LDS read might alias (it would wait for them
+// right away); completion is tracked only through vmcnt by the caller (sync_copies).
+// `base` and `lds` must be wave-uniform.
+__device__ __forceinline__ u32x4 copy_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void copy16_to_lds(u32x4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               : : "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void copy4_to_lds(u32x4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               : : "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
+}
+// Wait until at most N of this wave's asynchronous copies are in flight (they complete in
+// issue order) and its LDS operations are done, then join the workgroup barrier.
+template <int N>
+__device__ __forceinline__ void sync_copies() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// copy_tile_to_lds with the asynchronous copies above.
+template <int D, int R, int NW>
+__device__ __forceinline__ void copy_tile_async(unsigned char* dst, u32x4 rs, int stride,
+                                                int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int ITER = R * CPR / 64 / NW;
+#pragma unroll
+  for (int i = 0; i < ITER; ++i) {
+    const int p0 = (i * NW + wave) * 64;
+    const int pos = p0 + lane;
+    const int row = pos / CPR, pc = pos % CPR;
+    const int col = (pc ^ swz_f<D>(row)) * 8;
+    copy16_to_lds(rs, (uint32_t)((row * stride + col) * 2), lds_addr(dst + p0 * 16));
+  }
+}
 
 // Wait for every vector-memory operation except the most recent N. The counter retires in
 // issue order, so older loads are complete while the newest N (atomics) stay in flight.

@@ -153,6 +153,12 @@ fwd_kernel(FwdArgs a) {
       for (int s = 0; s < T::DS; ++s) qf[qb][s] = V8{};
     }
   }
+  // Consume the Q loads before the tile loop: otherwise the compiler keeps waiting for them
+  // inside the loop, where its vmcnt waits would also wait for the K/V copies in flight.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int s = 0; s < T::DS; ++s) asm volatile("" ::"v"(qf[qb][s]));
 
   const int kend = CAUSAL ? min(Sk, qt0 + T::BM) : Sk;
   const int ntiles = (kend + T::BN - 1) / T::BN;
@@ -167,16 +173,16 @@ fwd_kernel(FwdArgs a) {
   auto load_k = [&](int t, int buf) {
     const int kb0 = t * T::BN;
     const int rows = min(T::BN, Sk - kb0);
-    copy_tile_to_lds<D, T::BN, NW>(smem + buf * T::TBYTES,
-                                   make_rsrc(K + (int64_t)kb0 * a.k_ss, (uint32_t)((rows - 1) * a.k_ss + D) * 2u),
-                                   (int)a.k_ss, wave, lane);
+    copy_tile_async<D, T::BN, NW>(smem + buf * T::TBYTES,
+                                  copy_rsrc(K + (int64_t)kb0 * a.k_ss, (uint32_t)((rows - 1) * a.k_ss + D) * 2u),
+                                  (int)a.k_ss, wave, lane);
   };
   auto load_v = [&](int t, int buf) {
     const int kb0 = t * T::BN;
     const int rows = min(T::BN, Sk - kb0);
-    copy_tile_to_lds<D, T::BN, NW>(smem + V_OFF + buf * T::TBYTES,
-                                   make_rsrc(V + (int64_t)kb0 * a.v_ss, (uint32_t)((rows - 1) * a.v_ss + D) * 2u),
-                                   (int)a.v_ss, wave, lane);
+    copy_tile_async<D, T::BN, NW>(smem + V_OFF + buf * T::TBYTES,
+                                  copy_rsrc(V + (int64_t)kb0 * a.v_ss, (uint32_t)((rows - 1) * a.v_ss + D) * 2u),
+                                  (int)a.v_ss, wave, lane);
   };
   // Per-lane LDS bases. K row reads: key kb*32 + l32, 16-byte chunk 2*ds + half. V^T
   // transposed reads: keys 16kk + 4*half + (j16>>2) + 8*sec, d = db*32 + 16*(grp&1) +
@@ -411,8 +417,7 @@ fwd_kernel(FwdArgs a) {
     load_v(0, 0);
   }
   if (ntiles > 1) load_k(1, 1);
-  wait_vmem();
-  __syncthreads();
+  sync_copies<0>();
   if (ntiles > 0) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -450,8 +455,8 @@ fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) update_max(qb, mt[qb]);
     }
-    wait_vmem();      // this wave's part of K_{t+2} and V_{t+1} has landed in LDS
-    __syncthreads();  // ... every wave's part; every wave is done with K_{t+1} and V_t
+    sync_copies<0>();  // every wave's part of K_{t+2} and V_{t+1} has landed in LDS; every
+                       // wave is done with K_{t+1} and V_t
   };
 
   using F = bool_c<false>;

@@ -77,6 +77,8 @@ hipError_t launch_fwd_tail(const FwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_delta(const BwdArgs& a, int head_dim, int dtype, bool varlen, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, int dtype, bool causal, int mask_mode,
                       bool varlen, bool fused_dq, hipStream_t s);
+hipError_t launch_bwd_kv(const BwdArgs& a, int head_dim, int dtype, bool causal, int mask_mode,
+                         bool varlen, hipStream_t s);  // pipelined dK/dV kernel (default)
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int dtype, bool causal, int mask_mode,
                          bool varlen, hipStream_t s);
 hipError_t launch_q_tail(const BwdArgs& a, int head_dim, hipStream_t s);

@@ -221,10 +221,13 @@ int exattn_timing_read(const char** names, double* total_ms, int* launches, int 
  * max grows, 2 = 4 waves x 64 rows (lazy), one wave per SIMD; 2 applies to
  * head_dim 128 without a mask or cu_seqlens, other problems fall back to 0. `kernel` 1 =
  * backward:
- * 0 (default) = a dK/dV kernel (one workgroup per block of keys) and a separate dQ kernel
- * (one workgroup per block of query rows, recomputing P and dP), no atomics, bitwise
+ * 0 (default) = a dK/dV kernel (one workgroup per block of keys, the wave computing dS and
+ * dK one query tile behind the wave computing P and dV) and a separate dQ kernel (one
+ * workgroup per block of query rows, recomputing P and dP), no atomics, bitwise
  * reproducible; 1 = one fused kernel that adds dQ partial products into an fp32 workspace
- * accumulator with atomics, followed by a conversion pass (needs a larger workspace).
+ * accumulator with atomics, followed by a conversion pass (needs a larger workspace);
+ * 2 = as 0 with a dK/dV kernel whose two waves per key group work on the same query tile,
+ * two barriers per tile.
  * Every variant computes the same function up to fp32 rounding. Process-wide; not
  * thread-safe against concurrent calls. Returns EXATTN_ERR_SHAPE for an unknown kernel or
  * variant.

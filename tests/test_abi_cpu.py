@@ -199,10 +199,12 @@ def test_set_variant(lib):
     assert lib.exattn_set_variant(0, 3) == 4
     p = _problem()
     ws = {}
-    for v in (1, 0):
+    for v in (1, 2, 0):
         assert lib.exattn_set_variant(1, v) == 0
         ws[v] = lib.exattn_bwd_workspace_size(ctypes.byref(p))
     # the fused variant also needs the fp32 dQ accumulator [rows_q, H, D]
     assert ws[1] >= ws[0] + 2 * 100 * 4 * 128 * 4
-    assert lib.exattn_set_variant(1, 2) == 4
+    # the two split variants share the workspace layout
+    assert ws[2] == ws[0]
+    assert lib.exattn_set_variant(1, 3) == 4
     assert lib.exattn_set_variant(7, 0) == 4

@@ -81,3 +81,23 @@ def test_lazy_rescale_not_worse_than_eager(variant, s):
     for n in ("out", "lse"):
         say(f"  s={s} {n}: lazy {errs[0][n]:.3e} eager {errs[1][n]:.3e}")
         assert errs[0][n] <= 1.1 * errs[1][n] + 1e-4, n
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[c["name"] for c in BWD_CASES])
+def test_two_barrier_backward_variant(variant, case):
+    """Backward variant 2 (both waves of a key group on the same query tile) matches the
+    oracle; it shares the dQ kernel with the default, so dq is bitwise the same. Its dk and
+    dv sum the same products in the same order as the default's pipelined kernel, which
+    hands P to the dS product rounded to the input format (the two-barrier kernel hands it
+    over in fp32), so dk differs by about that rounding."""
+    p = case["make"]()
+    ref = run_oracle(p)
+    base = run_gpu(p)
+    variant(1, 2)
+    two = run_gpu(p)
+    compare(two, ref, tag=f"bwd two-barrier {case['name']}")
+    assert torch.equal(two["dq"], base["dq"])
+    for n in ("dk", "dv"):
+        d = (two[n].double() - base[n].double()).norm() / base[n].double().norm().clamp_min(1e-30)
+        say(f"  {case['name']} {n}: default vs two-barrier rel-L2 {d:.2e}")
+        assert d <= 4e-3, n
