@@ -4,16 +4,19 @@
 // 128 keys (four groups of 32) of one (unit, kv head), looping over every query head of the
 // group and every 64-row query tile that can see the block; per key group one wave pair,
 // both waves on one SIMD:
-//   wave A: S = Q K^T, P = exp2(min(S*c + bias - lse2, 0)) (hidden entries 0), P -> LDS
-//           (fp32), dV += P^T dO;                       keeps K fragments and dV in registers
+//   wave A: S = Q K^T, P = exp2(min(S*c + bias - lse2, 0)) (hidden entries 0), dV += P^T dO;
+//           keeps K fragments and dV in registers; P goes to LDS as the bf16 (fp16) operand
+//           fragments of its own dV product
 //   wave B: dS = P * (dP - Delta) with P from LDS, dK += dS^T Q, dP = dO V^T;
-//                                                       keeps V fragments and dK in registers
+//           keeps V fragments and dK in registers
 // Wave B runs one tile behind wave A: in the phase where A forms S and P of tile t and
 // adds dV, B forms dS and adds dK of tile t - 1 and computes dP of tile t (held in
 // registers into the next phase). So while A spends the VALU on the exponentials, B keeps
 // the SIMD's matrix unit busy, and one barrier per tile suffices. The buffers are rings
-// sized for that lag: Q x3 (B still reads tile t - 1 while tile t + 1 arrives), dO x2,
-// P x2, lse2 / Delta x3. Tile t + 1 is copied global -> LDS directly during phase t.
+// sized for that lag and for copies two tiles ahead: Q x4 (B still reads tile t - 1 while
+// tiles t + 1 and t + 2 arrive), dO x3, P x2, lse2 / Delta x3. Tiles and their lse2 and
+// Delta rows are copied global -> LDS with asynchronous copies; each phase ends with one
+// wait that leaves only the copies of tile t + 2 in flight, then the barrier.
 //
 // Sources: dv = P^T dO and dk = dS^T q (flash-dmattn PR #122 "Fix NaN/Inf values in dV
 // gradients during backward pass", section "Solution", item 2); P = exp(s - lse) from the

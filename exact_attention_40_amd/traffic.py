@@ -19,7 +19,7 @@ import sys
 
 KERNELS = {  # library timing name -> kernel template name (rocprofv3 may or may not demangle)
     "exattn_fwd_kernel": "fwd_kernel",
-    "exattn_bwd_dkdv_kernel": "bwd_kernel",
+    "exattn_bwd_dkdv_kernel": "bwd_kv_kernel",
     "exattn_bwd_dq_kernel": "bwd_dq_kernel",
     "exattn_bwd_delta_kernel": "delta_kernel",
     "exattn_fwd_fp8_kernel": "fwd_fp8_kernel",
