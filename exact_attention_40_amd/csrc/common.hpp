@@ -163,12 +163,17 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // treat them as LDS writes that every later LDS read might alias (it would wait for them
 // right away); completion is tracked only through vmcnt by the caller (sync_copies).
 // `base` and `lds` must be wave-uniform.
+// The descriptor and the LDS address go to scalar registers (readfirstlane: the values are
+// wave-uniform, and the instruction takes them from SGPRs).
+__device__ __forceinline__ uint32_t sgpr(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
 __device__ __forceinline__ u32x4 copy_rsrc(const void* base, uint32_t bytes) {
   const uint64_t p = reinterpret_cast<uint64_t>(base);
-  return u32x4{(uint32_t)p, (uint32_t)(p >> 32) & 0xffffu, bytes, 0x00020000u};
+  return u32x4{sgpr((uint32_t)p), sgpr((uint32_t)(p >> 32) & 0xffffu), sgpr(bytes), 0x00020000u};
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+  return sgpr((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
 }
 __device__ __forceinline__ void copy16_to_lds(u32x4 rsrc, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
