@@ -101,3 +101,34 @@ def test_two_barrier_backward_variant(variant, case):
         d = (two[n].double() - base[n].double()).norm() / base[n].double().norm().clamp_min(1e-30)
         say(f"  {case['name']} {n}: default vs two-barrier rel-L2 {d:.2e}")
         assert d <= 4e-3, n
+
+
+# (B, Sq, Sk, H, Hkv, D, causal): the default dK/dV kernel runs one phase per (query head of
+# the group, query tile) plus one; these walk 1 to 6 phases, with a ragged last query tile,
+# a partial key block and causal starts, where the ring slots and the tile-two-ahead copies
+# wrap differently.
+PHASE_CASES = [
+    (1, 64, 200, 1, 1, 128, False),    # 1 tile: no copy ahead at all
+    (1, 64, 200, 2, 1, 128, False),    # 2 tiles (two heads of a group)
+    (1, 150, 200, 1, 1, 128, False),   # 3 tiles, the last one 22 rows
+    (2, 100, 77, 4, 2, 64, False),     # 4 tiles, D = 64
+    (1, 130, 130, 2, 1, 128, True),    # causal: 6 tiles for keys 0..127, 2 for keys 128, 129
+    (1, 300, 260, 3, 1, 128, True),    # causal GQA 3:1, 15 tiles for the first key block
+]
+
+
+@pytest.mark.parametrize("case", PHASE_CASES, ids=lambda c: "B{}_Sq{}_Sk{}_H{}_Hkv{}_D{}_{}".format(
+    *c[:6], "causal" if c[6] else "full"))
+def test_dkdv_phase_counts(variant, case):
+    """The pipelined dK/dV kernel (default) matches the oracle and the two-barrier kernel
+    (variant 2) on short tile sequences."""
+    B, Sq, Sk, H, Hkv, D, causal = case
+    p = workloads.dense(B, Sq, Sk, H, Hkv, D, seed=7100 + Sq + Sk + H, causal=causal)
+    ref = run_oracle(p)
+    base = run_gpu(p)
+    compare(base, ref, tag=f"phases {case}")
+    variant(1, 2)
+    two = run_gpu(p)
+    for n in ("dk", "dv"):
+        d = (two[n].double() - base[n].double()).norm() / base[n].double().norm().clamp_min(1e-30)
+        assert d <= 4e-3, (n, float(d))
