@@ -677,58 +677,72 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
     constexpr int KO = BUF * T::TBYTES;
     if (t + 1 < ntiles) load_tile(t + 1, BUF ^ 1);
     // S^T and dP^T: K and V row fragments read four MFMAs ahead (fences keep the order).
+    // Unmasked tiles take the key blocks one after the other, and the VALU work of a block
+    // (P and dS) is issued between MFMAs that do not depend on it: block 0's between the S
+    // and dP MFMAs of block 1, block 1's between the dQ MFMAs of block 0. Masked tiles
+    // (mask reads, boundary tests) keep all VALU work after the S and dP MFMAs.
     f32x16 s[T::KB], dp[T::KB];
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb) s[kb] = dp[kb] = f32x16{};
+    const int kb0 = t * T::BN;
+    auto ds_elem = [&](int kb, int r) {
+      float p;
+      if constexpr (!MASKED) {
+        p = fast_exp2(min0(fmaf(s[kb][r], c2, -l2)));
+      } else {
+        const int kj = kb0 + kb * 32 + acc_row(r, half);
+        bool vis = (kj < Sk) && (qi < Sq);
+        if (CAUSAL) vis = vis && (kj <= qi);
+        float b2 = 0.f;
+        if (MASK != kMaskNone) {
+          const int64_t mi = m_base + (int64_t)min(qi, Sq - 1) * a.m_si + min(kj, Sk - 1);
+          if (MASK == kMaskBool) {
+            vis = vis && (mask_u8[mi] != 0);
+          } else {
+            const float bias = (float)mask_bf[mi];
+            vis = vis && (bias != -INFINITY);
+            b2 = vis ? bias * kLog2e : 0.f;
+          }
+        }
+        const float e2 = fast_exp2(min0(fmaf(s[kb][r], c2, b2 - l2)));
+        p = vis ? e2 : 0.f;
+      }
+      dp[kb][r] = p * (dp[kb][r] - dl);
+    };
+    static_assert(T::KB == 2, "two key blocks per tile");
     {
-      constexpr int NF = T::DS * T::KB * 2;    // (ds, kb, K or V)
+      constexpr int NF = T::DS * T::KB * 2;    // (kb, ds, K or V) unmasked; (ds, kb, K or V) masked
+      constexpr int EPM = 16 / (2 * T::DS);    // block-0 elements per block-1 MFMA
+      auto fkb = [](int f) { return MASKED ? (f / 2) % T::KB : f / (2 * T::DS); };
+      auto fds = [](int f) { return MASKED ? f / (2 * T::KB) : (f / 2) % T::DS; };
       auto frag = [&](int f) {
-        const int ds = f / (2 * T::KB), kb = (f / 2) % T::KB, isv = f & 1;
-        return lds_at<V8>(ar[ds], isv * V_OFF + KO + kb * 32 * RB);
+        return lds_at<V8>(ar[fds(f)], (f & 1) * V_OFF + KO + fkb(f) * 32 * RB);
       };
       V8 fr[4] = {frag(0), frag(1), frag(2), frag(3)};
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        const int ds = f / (2 * T::KB), kb = (f / 2) % T::KB;
+        const int ds = fds(f), kb = fkb(f);
         if (f & 1) dp[kb] = mfma32(fr[f % 4], df[ds], dp[kb]);
         else s[kb] = mfma32(fr[f % 4], qf[ds], s[kb]);
         if (f + 4 < NF) fr[f % 4] = frag(f + 4);
+        if (!MASKED && kb == 1) {
+#pragma unroll
+          for (int e = 0; e < EPM; ++e) ds_elem(0, (f - 2 * T::DS) * EPM + e);
+        }
         __builtin_amdgcn_sched_barrier(0x0004);
       }
     }
-    const int kb0 = t * T::BN;
+    if constexpr (MASKED) {
 #pragma unroll
-    for (int kb = 0; kb < T::KB; ++kb) {
+      for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p;
-        if constexpr (!MASKED) {
-          p = fast_exp2(min0(fmaf(s[kb][r], c2, -l2)));
-        } else {
-          const int kj = kb0 + kb * 32 + acc_row(r, half);
-          bool vis = (kj < Sk) && (qi < Sq);
-          if (CAUSAL) vis = vis && (kj <= qi);
-          float b2 = 0.f;
-          if (MASK != kMaskNone) {
-            const int64_t mi = m_base + (int64_t)min(qi, Sq - 1) * a.m_si + min(kj, Sk - 1);
-            if (MASK == kMaskBool) {
-              vis = vis && (mask_u8[mi] != 0);
-            } else {
-              const float bias = (float)mask_bf[mi];
-              vis = vis && (bias != -INFINITY);
-              b2 = vis ? bias * kLog2e : 0.f;
-            }
-          }
-          const float e2 = fast_exp2(min0(fmaf(s[kb][r], c2, b2 - l2)));
-          p = vis ? e2 : 0.f;
-        }
-        dp[kb][r] = p * (dp[kb][r] - dl);
-      }
+        for (int r = 0; r < 16; ++r) ds_elem(kb, r);
     }
     // dQ^T += K^T dS^T over 16-key slabs; the next slab's transposed K fragments are read
     // while this slab's MFMAs run.
     {
       constexpr int NKK = T::BN / 16;
+      constexpr int EPM = 16 / (2 * T::DB);    // block-1 elements per block-0 dQ MFMA
       V4 tb[2][T::DB][2];
       auto tload = [&](int kk, int slot) {
 #pragma unroll
@@ -747,6 +761,10 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int db = 0; db < T::DB; ++db) {
           dq[db] = mfma32(cat44(tb[kk & 1][db][0], tb[kk & 1][db][1]), sb, dq[db]);
+          if (!MASKED && kb == 0) {
+#pragma unroll
+            for (int e = 0; e < EPM; ++e) ds_elem(1, ((kk & 1) * T::DB + db) * EPM + e);
+          }
           __builtin_amdgcn_sched_barrier(0x0004);
         }
       }
