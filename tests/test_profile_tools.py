@@ -1,0 +1,60 @@
+"""The counter summary's normalisation on synthetic rocprofv3 counter files with known
+answers (no GPU): held clock from GRBM_GUI_ACTIVE summed over 8 XCDs, MFMA busy from
+SQ_VALU_MFMA_BUSY_CYCLES summed over 4 SIMDs per CU, LDS activity and read bandwidth per CU.
+"""
+
+import csv
+import os
+
+from exact_attention_40_amd import counter_summary
+
+FIELDS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
+          "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
+          "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Counter_Name",
+          "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+KNAME = "_ZN6exattn13bwd_dq_kernelIDF16bLi128ELb0ELi0ELb0EEEvNS_7BwdArgsE"
+
+
+def _write(path, counters, cus, clock_hz, dur_s, dispatches=3):
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for d in range(1, dispatches + 1):
+            start = 10**9 * d
+            end = start + int(dur_s * 1e9)
+            cycles = clock_hz * dur_s
+            for name, per_cycle in counters.items():
+                if name == "GRBM_GUI_ACTIVE":
+                    value = cycles * 8                       # summed over the XCDs
+                elif name == "SQ_VALU_MFMA_BUSY_CYCLES":
+                    value = per_cycle * cycles * 4 * cus     # summed over the SIMDs
+                elif name == "SQ_INSTS_LDS_LOAD_BANDWIDTH":
+                    value = per_cycle * cycles * cus / 64    # 64-byte units
+                else:
+                    value = per_cycle * cycles * cus         # summed over the CUs
+                row = {k: 0 for k in FIELDS}
+                row.update(Dispatch_Id=d, Kernel_Name=KNAME, Counter_Name=name,
+                           Counter_Value=value, Start_Timestamp=start, End_Timestamp=end)
+                w.writerow(row)
+
+
+def test_counter_summary_normalisation(tmp_path, monkeypatch):
+    cus, clk, dur = 256, 1.8e9, 2.5e-3
+    _write(tmp_path / "util", {"GRBM_GUI_ACTIVE": 1, "SQ_VALU_MFMA_BUSY_CYCLES": 0.625,
+                               "SQ_BUSY_CYCLES": 1}, cus, clk, dur)
+    _write(tmp_path / "lds", {"GRBM_GUI_ACTIVE": 1, "SQ_LDS_IDX_ACTIVE": 0.375,
+                              "SQ_INSTS_LDS_LOAD_BANDWIDTH": 96.0, "SQ_LDS_BANK_CONFLICT": 0},
+           cus, clk, dur)
+    out = tmp_path / "out.md"
+    monkeypatch.setattr("sys.argv", ["x", str(tmp_path), str(out), str(cus)])
+    counter_summary.main()
+    row = [l for l in out.read_text().splitlines() if l.startswith("| exattn_bwd_dq_kernel")]
+    assert len(row) == 1
+    cells = [c.strip() for c in row[0].strip("|").split("|")]
+    assert cells[1] == "2.500"                 # ms
+    assert cells[2] == "1.80"                  # held clock, GHz
+    assert cells[3] == "62.5%"                 # MFMA busy
+    assert cells[4] == f"{cus * 4096 * 1.8e9 / 1e12:.0f}"   # peak at the held clock
+    assert cells[5] == "37.5%"                 # LDS active
+    assert cells[6] == "96.0"                  # LDS read bytes per clock per CU
