@@ -71,7 +71,7 @@ def round_e4m3(x):
 
 def fp8_forward(q8, k8, v8, q_descale, k_descale, v_descale, *, causal=False, scale=None,
                 block_n=64, group_rows=32, tau=8.0, bound=16.0, quantize_p=True,
-                return_stats=False, units=None, row_groups=None):
+                return_stats=False, units=None, row_groups=None, cap_from="running_max"):
     """fp8 attention forward, tile by tile as the FlyDSL fp8 helper does (see module doc).
 
     q8 [B, Sq, H, D], k8 / v8 [B, Sk, Hkv, D]: float arrays holding e4m3 values (decoded,
@@ -79,11 +79,16 @@ def fp8_forward(q8, k8, v8, q_descale, k_descale, v_descale, *, causal=False, sc
     ``bound=None`` rebases onto the tile max without a cap (the behaviour before the fix);
     ``quantize_p=False`` skips the e4m3 rounding of P (then the result is the exact
     attention of the dequantised inputs, whatever the rebase sequence).
+    ``cap_from`` picks the reading of the cap: "running_max" (the default) bounds the base
+    at `bound` below the row's running max; "previous_base" bounds each rebase at `bound`
+    below the base it replaces, so successive drops can add up.
     With ``return_stats`` a dict counts triggered tiles and rebases that lowered a base,
     and those the cap limited. ``units`` (a list of (b, h)) and ``row_groups`` (indices of
     groups of ``group_rows`` rows) restrict the work; entries left out are NaN. A group's
     rows share every decision, so a group is computed whole or not at all.
     """
+    if cap_from not in ("running_max", "previous_base"):
+        raise ValueError(cap_from)
     q8, k8, v8 = (np.asarray(t, dtype=np.float64) for t in (q8, k8, v8))
     B, Sq, H, D = q8.shape
     Sk, Hkv = k8.shape[1], k8.shape[2]
@@ -125,13 +130,19 @@ def fp8_forward(q8, k8, v8, q_descale, k_descale, v_descale, *, causal=False, sc
             np.logical_or.at(fire_grp, group, fire_row)
             fire = fire_grp[group]
             # 2. rebase: onto the row's tile max, never more than `bound` below its
-            #    running max
+            #    running max (or below its previous base)
             if fire.any():
                 stats["triggers"] += int(fire_grp.sum())
-                m_new = m_tile if bound is None else np.maximum(m_tile, m_max - bound)
+                if bound is None:
+                    m_new = m_tile
+                    floor = np.full(n, -np.inf)
+                elif cap_from == "running_max":
+                    floor = m_max - bound
+                else:
+                    floor = np.where(m == -np.inf, -np.inf, m - bound)
+                m_new = np.maximum(m_tile, floor)
                 stats["lowered"] += int(np.sum(fire & (m_new < m)))
-                if bound is not None:
-                    stats["capped"] += int(np.sum(fire & (m_tile < m_max - bound)))
+                stats["capped"] += int(np.sum(fire & (m_tile < floor)))
                 with np.errstate(over="ignore", invalid="ignore"):
                     corr = np.where(m == -np.inf, 1.0, np.exp2(m - m_new))
                 corr = np.where(fire, corr, 1.0)

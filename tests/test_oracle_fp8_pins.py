@@ -213,3 +213,24 @@ def test_page_fp8_table_wide_range_v_ones():
             with np.errstate(all="ignore"):
                 free, _ = fp8_forward(q, k, v, p.q_descale, p.k_descale, p.v_descale, bound=None)
             assert not np.all(np.isfinite(free))
+
+
+def test_cap_reading_pinned_by_page_table():
+    """Which base the cap of 16 is measured from. FlyDSL PR #1033, "The fp8 helper, second
+    commit" (tests/golden/page_values.json, fp8_bound_table) reports zero NaN elements with
+    bound 16 at K x 1000, 5000 and 20000, V = ones, S = 12288. On that workload (four
+    32-row decision groups, 12288 keys) the cap measured from the row's running max keeps
+    every output finite, while a cap measured from the previous base lets the drops of
+    successive rebases add up and overflows; so the page's table rules out the second
+    reading."""
+    g = GOLDEN["fp8_bound_table"]
+    assert g["bound_16_nan_elements"] == [0, 0, 0]
+    for km in g["k_scale"]:
+        p = workloads.fp8_dense(1, 128, 12288, 2, 1, 128, seed=37, k_mult=float(km), v_ones=True)
+        q, k, v = p.decoded()
+        out, _ = fp8_forward(q, k, v, p.q_descale, p.k_descale, p.v_descale, cap_from="running_max")
+        assert np.all(np.isfinite(out)), km
+        with np.errstate(all="ignore"):
+            prev, _ = fp8_forward(q, k, v, p.q_descale, p.k_descale, p.v_descale,
+                                  cap_from="previous_base")
+        assert not np.all(np.isfinite(prev)), km
