@@ -13,7 +13,7 @@ import threading
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libexattn.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 OK = 0
 STATUS_NAMES = {
@@ -29,7 +29,7 @@ MASK_NONE, MASK_BOOL_U8, MASK_ADD_BF16 = 0, 1, 2
 EXPORTED = (
     "exattn_abi_version", "exattn_check", "exattn_fwd", "exattn_fwd_fp8", "exattn_bwd_workspace_size",
     "exattn_bwd", "exattn_status_string", "exattn_last_error", "exattn_timing_enable",
-    "exattn_timing_read", "exattn_set_variant",
+    "exattn_timing_read",
 )
 
 _i32, _i64, _f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
@@ -44,7 +44,8 @@ class Problem(ctypes.Structure):
         ("q_stride", _i64 * 3), ("k_stride", _i64 * 3), ("v_stride", _i64 * 3),
         ("o_stride", _i64 * 3), ("do_stride", _i64 * 3), ("mask_stride", _i64 * 4),
         ("mask", _vp), ("cu_seqlens_q", _vp), ("cu_seqlens_k", _vp),
-        ("num_seqs", _i32), ("max_seqlen_q", _i32), ("max_seqlen_k", _i32), ("reserved", _i32),
+        ("num_seqs", _i32), ("max_seqlen_q", _i32), ("max_seqlen_k", _i32),
+        ("fwd_variant", _i32), ("bwd_variant", _i32), ("reserved", _i32),
     ]
 
 
@@ -87,8 +88,6 @@ def load():
         lib.exattn_timing_read.argtypes = [ctypes.POINTER(ctypes.c_char_p),
                                            ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_int), ctypes.c_int]
-        lib.exattn_set_variant.restype = ctypes.c_int
-        lib.exattn_set_variant.argtypes = [ctypes.c_int, ctypes.c_int]
         v = lib.exattn_abi_version()
         if v != ABI_VERSION:
             raise RuntimeError(f"libexattn ABI version {v}, binding expects {ABI_VERSION}")

@@ -20,7 +20,7 @@ import torch
 from . import _lib
 
 __all__ = ["exattn_fwd", "exattn_fwd_fp8", "exattn_bwd", "exattn_check", "attn_fwd", "attn_bwd", "attention",
-           "AttnFunction", "timing_enable", "timing_read", "workspace_size", "set_variant"]
+           "AttnFunction", "timing_enable", "timing_read", "workspace_size"]
 
 
 def _fail(lib, status):
@@ -50,7 +50,7 @@ class _Spec:
     """Validated shapes and options of one call."""
 
     def __init__(self, q, k, v, causal, scale, mask, cu_seqlens_q, cu_seqlens_k,
-                 max_seqlen_q, max_seqlen_k):
+                 max_seqlen_q, max_seqlen_k, fwd_variant=0, bwd_variant=0):
         for name, t in (("q", q), ("k", k), ("v", v)):
             if not isinstance(t, torch.Tensor):
                 raise ValueError(f"{name} must be a tensor")
@@ -97,6 +97,7 @@ class _Spec:
         self.mask = mask
         self.cu_q, self.cu_k = cu_seqlens_q, cu_seqlens_k
         self.max_q, self.max_k = max_seqlen_q, max_seqlen_k
+        self.fwd_variant, self.bwd_variant = int(fwd_variant), int(bwd_variant)
 
     @property
     def q_shape(self):
@@ -148,11 +149,8 @@ class _Spec:
                 if cu.dtype != torch.int32:
                     raise ValueError(f"{name} must be int32")
                 if cu.device.type == "cpu":
-                    c = cu.tolist()
-                    if c[0] != 0 or any(b < a for a, b in zip(c, c[1:])) or c[-1] > total:
-                        raise ValueError(f"{name} must start at 0, be non-decreasing and end "
-                                         f"at most at {total}")
-                    longest = max(b - a for a, b in zip(c, c[1:]))
+                    given = max_q if name == "cu_seqlens_q" else max_k
+                    longest = _host_cu_longest(cu.tolist(), total, name, given)
                     if name == "cu_seqlens_q":
                         max_q = longest if max_q is None else max_q
                     else:
@@ -193,7 +191,22 @@ class _Spec:
         p.num_seqs = nseq
         p.max_seqlen_q = max_q or 0
         p.max_seqlen_k = max_k or 0
+        p.fwd_variant = self.fwd_variant
+        p.bwd_variant = self.bwd_variant
         return p
+
+
+def _host_cu_longest(c, total, name, given):
+    """Check host cu_seqlens offsets `c` against `total` packed rows and return the longest
+    sequence. A given max_seqlen below it is rejected: the library would truncate that
+    sequence (include/exattn.h, packed sequences)."""
+    if c[0] != 0 or any(b < a for a, b in zip(c, c[1:])) or c[-1] > total:
+        raise ValueError(f"{name} must start at 0, be non-decreasing and end at most at {total}")
+    longest = max(b - a for a, b in zip(c, c[1:]))
+    if given is not None and given < longest:
+        raise ValueError(f"max_seqlen_{name[-1]}={given} is below the longest sequence "
+                         f"({longest}): its rows past {given} would not be computed")
+    return longest
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -216,7 +229,7 @@ def exattn_check(q, k, v, *, causal=False, scale=None, mask=None, cu_seqlens_q=N
 
 
 def exattn_fwd(q, k, v, *, causal=False, scale=None, mask=None, cu_seqlens_q=None,
-               cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None
+               cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, variant=0
                ) -> Tuple[torch.Tensor, torch.Tensor]:
     """Forward attention: returns (out, lse).
 
@@ -225,10 +238,11 @@ def exattn_fwd(q, k, v, *, causal=False, scale=None, mask=None, cu_seqlens_q=Non
     lse [H, Tq]. q, k, v are bf16 or fp16 (all the same); out has their dtype.
     mask: bool (True = attend) or additive bf16 (for either input dtype), broadcastable to
     [B, H, Sq, Sk]. lse is the natural-log log-sum-exp; empty rows give out 0, lse -inf.
+    variant: the forward tiling for this call (fwd_variant in include/exattn.h).
     """
     lib = _lib.load()
     spec = _Spec(q, k, v, causal, scale, mask, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                 max_seqlen_k)
+                 max_seqlen_k, fwd_variant=variant)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device)
         with torch.cuda.stream(stream):
@@ -308,7 +322,7 @@ def workspace_size(q, k, v, **kw) -> int:
     lib = _lib.load()
     spec = _Spec(q, k, v, kw.get("causal", False), kw.get("scale"), kw.get("mask"),
                  kw.get("cu_seqlens_q"), kw.get("cu_seqlens_k"), kw.get("max_seqlen_q"),
-                 kw.get("max_seqlen_k"))
+                 kw.get("max_seqlen_k"), bwd_variant=kw.get("variant", 0))
     with torch.cuda.device(q.device):
         side = spec.prepare_side_inputs(q.device)
         p = spec.problem(_norm(q), _norm(k), _norm(v), side, out=_norm(q), dout=_norm(q))
@@ -316,15 +330,16 @@ def workspace_size(q, k, v, **kw) -> int:
 
 
 def exattn_bwd(q, k, v, out, dout, lse, *, causal=False, scale=None, mask=None,
-               cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None
-               ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+               cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None,
+               variant=0) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Backward attention: returns (dq, dk, dv) for the same options as the forward.
 
     out and lse must be the forward's outputs for these inputs; dout = dL/dout.
+    variant: the backward kernels for this call (bwd_variant in include/exattn.h).
     """
     lib = _lib.load()
     spec = _Spec(q, k, v, causal, scale, mask, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                 max_seqlen_k)
+                 max_seqlen_k, bwd_variant=variant)
     for name, t in (("out", out), ("dout", dout)):
         if not isinstance(t, torch.Tensor) or tuple(t.shape) != spec.q_shape:
             raise ValueError(f"{name} must have q's shape {spec.q_shape}, got "
@@ -390,14 +405,6 @@ def attention(q, k, v, causal=False, scale=None, mask=None, cu_seqlens_q=None,
     """Differentiable attention output (in q's dtype, bf16 or fp16)."""
     return AttnFunction.apply(q, k, v, causal, scale, mask, cu_seqlens_q, cu_seqlens_k,
                               max_seqlen_q, max_seqlen_k)
-
-
-def set_variant(kernel: int, variant: int):
-    """Select a compiled tiling (see exattn_set_variant in include/exattn.h)."""
-    lib = _lib.load()
-    st = lib.exattn_set_variant(int(kernel), int(variant))
-    if st != _lib.OK:
-        _fail(lib, st)
 
 
 def timing_enable(on: bool = True):

@@ -99,14 +99,23 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Strides are in elements; rows must start on 16-byte boundaries (8 elements of 2 bytes,
 // 16 of 1 byte).
-exattn_status check_strides(const int64_t* st, bool varlen, const char* name, int mult) {
+// Token strides are bounded so that a tile of up to 128 rows stays inside the kernels'
+// 32-bit buffer offsets (`max_token` elements).
+exattn_status check_strides(const int64_t* st, bool varlen, const char* name, int mult,
+                            int64_t max_token) {
   for (int i = varlen ? 1 : 0; i < 3; ++i) {
     if (st[i] < 0 || (st[i] % mult) != 0)
       return fail(EXATTN_ERR_STRIDE, "%s stride[%d] = %lld must be a non-negative multiple of %d",
                   name, i, (long long)st[i], mult);
   }
+  if (st[1] >= max_token)
+    return fail(EXATTN_ERR_STRIDE, "%s token stride %lld must be below %lld elements", name,
+                (long long)st[1], (long long)max_token);
   return EXATTN_OK;
 }
+
+constexpr int64_t kMaxTokenStride16 = int64_t(1) << 23;  // 16-bit inputs
+constexpr int64_t kMaxTokenStride8 = int64_t(1) << 24;   // fp8 inputs (64-row tiles)
 
 // bwd: also check the out/dout strides. fp8: the problem of exattn_fwd_fp8 (e4m3 inputs,
 // head_dim 128, dense, no mask).
@@ -133,6 +142,16 @@ exattn_status validate(const exattn_problem* p, bool bwd, bool fp8 = false) {
   if (p->seqlen_q < 0 || p->seqlen_k < 0)
     return fail(EXATTN_ERR_SHAPE, "negative sequence length");
   if (p->causal != 0 && p->causal != 1) return fail(EXATTN_ERR_SHAPE, "causal must be 0 or 1");
+  if (p->reserved != 0) return fail(EXATTN_ERR_SHAPE, "reserved must be 0");
+  if (fp8 && (p->fwd_variant != 0 || p->bwd_variant != 0))
+    return fail(EXATTN_ERR_SHAPE, "the fp8 forward has one tiling: fwd_variant and bwd_variant must be 0");
+  if (p->fwd_variant < 0 || p->fwd_variant > 2)
+    return fail(EXATTN_ERR_SHAPE, "unknown fwd_variant %d (0, 1 or 2)", p->fwd_variant);
+  if (p->bwd_variant < 0 || p->bwd_variant > 2)
+    return fail(EXATTN_ERR_SHAPE, "unknown bwd_variant %d (0, 1 or 2)", p->bwd_variant);
+  if ((int64_t)p->heads_q * p->head_dim >= kMaxTokenStride16 ||
+      (int64_t)p->heads_kv * p->head_dim >= kMaxTokenStride16)
+    return fail(EXATTN_ERR_SHAPE, "heads * head_dim must be below 2^23 elements");
   if (!std::isfinite(p->scale)) return fail(EXATTN_ERR_SCALE, "scale must be finite");
   const bool varlen = p->cu_seqlens_q != nullptr || p->cu_seqlens_k != nullptr;
   if (varlen) {
@@ -160,12 +179,13 @@ exattn_status validate(const exattn_problem* p, bool bwd, bool fp8 = false) {
   }
   exattn_status s;
   const int mult = fp8 ? 16 : 8;
-  if ((s = check_strides(p->q_stride, varlen, "q", mult)) != EXATTN_OK) return s;
-  if ((s = check_strides(p->k_stride, varlen, "k", mult)) != EXATTN_OK) return s;
-  if ((s = check_strides(p->v_stride, varlen, "v", mult)) != EXATTN_OK) return s;
+  const int64_t mt = fp8 ? kMaxTokenStride8 : kMaxTokenStride16;
+  if ((s = check_strides(p->q_stride, varlen, "q", mult, mt)) != EXATTN_OK) return s;
+  if ((s = check_strides(p->k_stride, varlen, "k", mult, mt)) != EXATTN_OK) return s;
+  if ((s = check_strides(p->v_stride, varlen, "v", mult, mt)) != EXATTN_OK) return s;
   if (bwd) {
-    if ((s = check_strides(p->o_stride, varlen, "out", 8)) != EXATTN_OK) return s;
-    if ((s = check_strides(p->do_stride, varlen, "dout", 8)) != EXATTN_OK) return s;
+    if ((s = check_strides(p->o_stride, varlen, "out", 8, mt)) != EXATTN_OK) return s;
+    if ((s = check_strides(p->do_stride, varlen, "dout", 8, mt)) != EXATTN_OK) return s;
   }
   // Size limits: row counts times heads must index within int32 rows, blocks within 2^31.
   const int64_t rows_q = varlen ? (int64_t)p->seqlen_q : (int64_t)p->batch * p->seqlen_q;
@@ -198,7 +218,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // selected.
 // The fused (atomic) backward is selected by variant 1 and exists for bf16 only.
 bool fused_backward(const exattn_problem* p) {
-  return get_bwd_variant() == 1 && p->dtype == EXATTN_DTYPE_BF16;
+  return p->bwd_variant == 1 && p->dtype == EXATTN_DTYPE_BF16;
 }
 
 struct WsLayout {
@@ -314,6 +334,8 @@ exattn_status exattn_fwd(const exattn_problem* p, const void* q, const void* k, 
   const int bm = fwd_block_m(D, p->mask_kind, g.varlen);
   const int maxq = g.varlen ? p->max_seqlen_q : p->seqlen_q;
   a.num_q_tiles = (maxq + bm - 1) / bm;
+  a.max_sq = maxq;
+  a.max_sk = g.varlen ? p->max_seqlen_k : p->seqlen_k;
   a.lse_row = p->seqlen_q;
   a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
   if ((int64_t)a.num_units * H * a.num_q_tiles > INT32_MAX)
@@ -322,7 +344,7 @@ exattn_status exattn_fwd(const exattn_problem* p, const void* q, const void* k, 
   hipError_t e;
   if (a.num_q_tiles > 0) {
     e = timed(KernelId::Fwd, s, [&] {
-      return launch_fwd(a, D, p->dtype, p->causal != 0, p->mask_kind, g.varlen, s);
+      return launch_fwd(a, D, p->dtype, p->causal != 0, p->mask_kind, g.varlen, p->fwd_variant, s);
     });
     if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
   }
@@ -378,6 +400,8 @@ exattn_status exattn_fwd_fp8(const exattn_problem* p, const void* q, const void*
   a.num_units = p->batch;
   const int bm = fwd_fp8_block_m();
   a.num_q_tiles = (p->seqlen_q + bm - 1) / bm;
+  a.max_sq = p->seqlen_q;
+  a.max_sk = p->seqlen_k;
   a.lse_row = p->seqlen_q;
   a.scale_log2 = (float)c2;
   a.v_descale = v_descale;
@@ -456,6 +480,8 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
   const int bmq = bwd_dq_block_m(D);
   const int maxq = g.varlen ? p->max_seqlen_q : p->seqlen_q;
   a.num_q_blocks = (maxq + bmq - 1) / bmq;
+  a.max_sq = maxq;
+  a.max_sk = maxk;
   a.lse_row = p->seqlen_q;
   a.rows_q = (int)g.rows_q;
   a.rows_k = (int)g.rows_k;
@@ -483,7 +509,7 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
   if (e != hipSuccess) return hip_fail(e, "delta kernel launch");
   const bool causal = p->causal != 0;
   if (a.num_k_blocks > 0) {
-    const bool pipelined = !fused && get_bwd_variant() != 2;
+    const bool pipelined = !fused && p->bwd_variant != 2;
     e = timed(fused ? KernelId::BwdFused : KernelId::BwdDkDv, s, [&] {
       return pipelined ? launch_bwd_kv(a, D, p->dtype, causal, p->mask_kind, g.varlen, s)
                        : launch_bwd(a, D, p->dtype, causal, p->mask_kind, g.varlen, fused, s);
@@ -506,19 +532,6 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
     if (e != hipSuccess) return hip_fail(e, "kv tail launch");
   }
   return EXATTN_OK;
-}
-
-exattn_status exattn_set_variant(int kernel, int variant) {
-  g_err[0] = 0;
-  if (kernel == 0 && variant >= 0 && variant <= 2) {
-    set_fwd_variant(variant);
-    return EXATTN_OK;
-  }
-  if (kernel == 1 && variant >= 0 && variant <= 2) {
-    set_bwd_variant(variant);
-    return EXATTN_OK;
-  }
-  return fail(EXATTN_ERR_SHAPE, "unknown kernel %d or variant %d", kernel, variant);
 }
 
 exattn_status exattn_timing_enable(int enable) {

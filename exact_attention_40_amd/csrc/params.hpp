@@ -24,6 +24,8 @@ struct FwdArgs {
   int num_units;     // batch (dense) or num_seqs (packed)
   int num_q_tiles;   // per unit
   int lse_row;       // packed: row count of lse ([H, lse_row]); dense: Sq
+  int max_sq;        // packed: sequences are truncated to max_sq query rows ...
+  int max_sk;        // ... and max_sk key rows (max_seqlen); dense: Sq and Sk
   float scale_log2;  // scale * log2(e); fp8 forward: scale * q_descale * k_descale * log2(e)
   float v_descale;   // fp8 forward only: multiplies the normalised output
 };
@@ -56,6 +58,8 @@ struct BwdArgs {
   int num_k_blocks;  // key blocks per (unit, kv head), dK/dV kernel
   int num_q_blocks;  // query blocks per (unit, head), dQ kernel
   int lse_row;
+  int max_sq;        // packed: sequences are truncated to max_sq query rows and max_sk key
+  int max_sk;        // rows (max_seqlen); dense: Sq and Sk
   int rows_q;        // rows of q per head in total: B*Sq (dense) or total_q (packed)
   int rows_k;
   int rotate;        // query-tile order: 0 = in order, 1 = spread by key block, 2 = offset kbi % 8
@@ -72,7 +76,7 @@ const char* kernel_name(KernelId id);
 
 // Launchers return hipGetLastError() after the launch. `variant` selects the tiling.
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, int dtype, bool causal, int mask_mode,
-                      bool varlen, hipStream_t s);
+                      bool varlen, int variant, hipStream_t s);
 hipError_t launch_fwd_tail(const FwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_delta(const BwdArgs& a, int head_dim, int dtype, bool varlen, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, int dtype, bool causal, int mask_mode,
@@ -89,13 +93,9 @@ constexpr int kMaxOrderedUnits = 8192;  // packed sequences ranked for the dK/dV
 hipError_t launch_unit_order(const BwdArgs& a, int32_t* order, hipStream_t s);
 hipError_t launch_fwd_fp8(const FwdArgs& a, bool causal, hipStream_t s);  // head_dim 128, dense
 
-// Tile shapes the host needs for grid sizing, and the tiling selectors.
+// Tile shapes the host needs for grid sizing.
 int fwd_block_m(int head_dim, int mask, bool varlen);
 int fwd_fp8_block_m();
-void set_fwd_variant(int v);
-void set_bwd_variant(int v);
-int get_bwd_variant();
-int get_fwd_variant();
 int bwd_block_n(int head_dim);
 int bwd_dq_block_m(int head_dim);
 

@@ -53,15 +53,17 @@
 extern "C" {
 #endif
 
-#define EXATTN_ABI_VERSION 1
+#define EXATTN_ABI_VERSION 2
 
 typedef enum exattn_status {
   EXATTN_OK = 0,
   EXATTN_ERR_NULL = 1,       /* a required pointer is NULL */
   EXATTN_ERR_DTYPE = 2,      /* dtype not accepted by the call (bf16/fp16; fp8 e4m3 for fp8) */
   EXATTN_ERR_HEAD_DIM = 3,   /* head_dim not in {64, 128} */
-  EXATTN_ERR_SHAPE = 4,      /* negative sizes, heads_q % heads_kv != 0, size overflow */
-  EXATTN_ERR_STRIDE = 5,     /* a stride is negative or not a multiple of 8 elements */
+  EXATTN_ERR_SHAPE = 4,      /* negative sizes, heads_q % heads_kv != 0, size overflow, an
+                                unknown variant or a non-zero reserved field */
+  EXATTN_ERR_STRIDE = 5,     /* a stride is negative, not a multiple of 8 elements, or too
+                                large for the kernels' 32-bit tile offsets (see below) */
   EXATTN_ERR_ALIGN = 6,      /* a q/k/v/out/dout/dq/dk/dv pointer is not 16-byte aligned */
   EXATTN_ERR_MASK = 7,       /* bad mask kind, NULL mask, negative mask stride, mask + varlen */
   EXATTN_ERR_VARLEN = 8,     /* num_seqs < 1, max_seqlen < 0, or one cu_seqlens pointer NULL */
@@ -108,6 +110,23 @@ typedef enum exattn_mask_kind {
  *
  * The mask (dense only) is indexed by element strides mask_stride = {b, h, i, j}; a stride
  * of 0 broadcasts that axis (key-broadcast and per-batch masks); mask_stride[3] must be 1.
+ *
+ * Size limits of the 16-bit (bf16/fp16) path: the kernels address a tile of up to 128 rows
+ * through 32-bit byte offsets, so every token stride (x_stride[1] of q, k, v, out, dout)
+ * and heads_q * head_dim and heads_kv * head_dim must be below 2^23 elements
+ * (EXATTN_ERR_STRIDE / EXATTN_ERR_SHAPE otherwise). The fp8 forward needs its token
+ * strides below 2^24 elements.
+ *
+ * Packed sequences with device offsets (the library never reads device memory on the
+ * host, so it cannot check them): the kernels clamp every offset into [0, seqlen_q] (or
+ * [0, seqlen_k]) and take sequence s as rows [c_s, max(c_s, c_{s+1})) of the clamped values,
+ * so no offset array makes a kernel read or write outside the tensors. A sequence longer
+ * than max_seqlen_q (max_seqlen_k) is truncated to its first max_seqlen_q query rows
+ * (max_seqlen_k key rows): attention is computed over the truncated sequence, and the rows
+ * and keys past the truncation are written like rows past cu_seqlens[num_seqs] (out 0,
+ * lse -inf, dq 0, dk 0, dv 0). Callers that want every row computed pass max_seqlen at
+ * least the longest sequence; the Python binding checks this whenever the offsets are on
+ * the host.
  */
 typedef struct exattn_problem {
   int32_t dtype;         /* exattn_dtype */
@@ -132,8 +151,28 @@ typedef struct exattn_problem {
   int32_t num_seqs;
   int32_t max_seqlen_q;
   int32_t max_seqlen_k;
-  int32_t reserved;
+  int32_t fwd_variant;   /* forward tiling for this call, 0 = default (see below) */
+  int32_t bwd_variant;   /* backward kernels for this call, 0 = default (see below) */
+  int32_t reserved;      /* must be 0 */
 } exattn_problem;
+
+/*
+ * Tilings (fwd_variant, bwd_variant), selected per call so that concurrent calls from
+ * different threads never see each other's choice. Every variant computes the same
+ * function up to fp32 rounding; they exist to compare designs.
+ *   fwd_variant 0 (default): 8 waves x 32 query rows per workgroup with the lazy rescale
+ *     (threshold 8 in log2 units; FlyDSL PR #1033, "The fix"); 1: the same tiling with an
+ *     eager rescale whenever a row max grows; 2: 4 waves x 64 rows, lazy, one wave per SIMD
+ *     (bf16, head_dim 128, no mask, dense; other problems run variant 0).
+ *   bwd_variant 0 (default): a dK/dV kernel (one workgroup per block of keys, the wave
+ *     computing dS and dK one query tile behind the wave computing P and dV) and a separate
+ *     dQ kernel (one workgroup per block of query rows, recomputing P and dP), no atomics,
+ *     bitwise reproducible; 1: one fused kernel that adds dQ partial products into an fp32
+ *     workspace accumulator with atomics, then a conversion pass (bf16 only, larger
+ *     workspace; fp16 problems run variant 0); 2: as 0 with a dK/dV kernel whose two waves
+ *     per key group work on the same query tile, two barriers per tile.
+ * Other values are rejected with EXATTN_ERR_SHAPE.
+ */
 
 /* ABI version of the loaded library (EXATTN_ABI_VERSION at build time). */
 int exattn_abi_version(void);
@@ -174,15 +213,19 @@ exattn_status exattn_fwd_fp8(const exattn_problem* p, const void* q, const void*
                              const void* v, float q_descale, float k_descale, float v_descale,
                              void* out, float* lse, void* stream);
 
-/* Bytes of device workspace exattn_bwd needs for this problem under the backward variant
- * selected at the time of the call (see exattn_set_variant; 0 on invalid input). */
+/* Bytes of device workspace exattn_bwd needs for this problem (its bwd_variant included):
+ * fp32 [lse * log2(e) | rowsum(dout * out)] per (row, head), an int32 ranking of the
+ * packed sequences, and for bwd_variant 1 the fp32 dQ accumulator. The workspace is the
+ * caller's memory, as every buffer is (NVIDIA cudnn-frontend PR #429, first commit
+ * message: the caller owns the scratch the backward needs and its zero-fill is enqueued on
+ * the launch stream). Returns 0 on invalid input. */
 size_t exattn_bwd_workspace_size(const exattn_problem* p);
 
 /*
  * Backward. q, k, v, out, dout: device inputs of the problem's dtype (strides in p); lse:
  * fp32 device input as written by exattn_fwd for the same problem (read only). dq, dk, dv:
- * device outputs of that dtype, contiguous, every element written. The fused variant (see
- * exattn_set_variant) applies to bf16 only; fp16 problems always take the default split
+ * device outputs of that dtype, contiguous, every element written. The fused variant
+ * (bwd_variant 1) applies to bf16 only; fp16 problems always take the default split
  * backward. workspace: device memory of at least
  * exattn_bwd_workspace_size(p) bytes, 256-byte aligned, owned by the caller; its contents
  * on entry do not matter and on exit are unspecified. Concurrent calls must not share a
@@ -198,10 +241,13 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
                          void* dk, void* dv, void* workspace, size_t workspace_bytes,
                          void* stream);
 
-/* Static description of a status code. */
+/* Static description of a status code. Rejections are reported as statuses instead of
+ * being run or silently accepted (cudnn-frontend PR #429, "Validate the input contract":
+ * an unsupported input fails loudly with a message). */
 const char* exattn_status_string(exattn_status s);
 
-/* Message of the last non-OK status returned on the calling thread ("" if none). */
+/* Message of the last non-OK status returned on the calling thread ("" if none): which
+ * argument was rejected and why (cudnn-frontend PR #429, "Validate the input contract"). */
 const char* exattn_last_error(void);
 
 /*
@@ -213,26 +259,6 @@ const char* exattn_last_error(void);
  */
 exattn_status exattn_timing_enable(int enable);
 int exattn_timing_read(const char** names, double* total_ms, int* launches, int max);
-
-/*
- * Tiling selection, for benchmarking the compiled alternatives. `kernel` 0 = forward:
- * variant 0 (default) = 8 waves x 32 query rows per workgroup with the lazy rescale
- * (threshold 8 in log2 units), 1 = the same tiling with an eager rescale whenever a row
- * max grows, 2 = 4 waves x 64 rows (lazy), one wave per SIMD; 2 applies to
- * head_dim 128 without a mask or cu_seqlens, other problems fall back to 0. `kernel` 1 =
- * backward:
- * 0 (default) = a dK/dV kernel (one workgroup per block of keys, the wave computing dS and
- * dK one query tile behind the wave computing P and dV) and a separate dQ kernel (one
- * workgroup per block of query rows, recomputing P and dP), no atomics, bitwise
- * reproducible; 1 = one fused kernel that adds dQ partial products into an fp32 workspace
- * accumulator with atomics, followed by a conversion pass (needs a larger workspace);
- * 2 = as 0 with a dK/dV kernel whose two waves per key group work on the same query tile,
- * two barriers per tile.
- * Every variant computes the same function up to fp32 rounding. Process-wide; not
- * thread-safe against concurrent calls. Returns EXATTN_ERR_SHAPE for an unknown kernel or
- * variant.
- */
-exattn_status exattn_set_variant(int kernel, int variant);
 
 #ifdef __cplusplus
 }

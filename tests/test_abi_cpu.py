@@ -117,6 +117,15 @@ def test_check_accepts_valid_problem(lib):
     (dict(cu_seqlens_q=4096, cu_seqlens_k=4096, num_seqs=2, max_seqlen_q=101), 8),
     (dict(cu_seqlens_q=4096, cu_seqlens_k=4096, num_seqs=2, max_seqlen_q=10, max_seqlen_k=10,
           mask_kind=1, mask=16), 7),           # mask + varlen
+    # token strides whose 128-row tile span would overflow the kernels' 32-bit offsets
+    (dict(q_stride=(0, 1 << 23, 128)), 5),
+    (dict(k_stride=(0, 1 << 23, 128)), 5),
+    (dict(v_stride=(0, (1 << 23) + 8, 128)), 5),
+    (dict(heads_q=65536, heads_kv=1), 4),      # heads * head_dim reaches 2^23
+    (dict(fwd_variant=3), 4),                  # per-call tiling selectors
+    (dict(fwd_variant=-1), 4),
+    (dict(bwd_variant=3), 4),
+    (dict(reserved=1), 4),
 ])
 def test_check_rejects(lib, kw, status):
     p = _problem(**kw)
@@ -193,18 +202,46 @@ def test_timing_read_empty(lib):
     assert lib.exattn_timing_enable(0) == 0
 
 
-def test_set_variant(lib):
-    for v in (1, 2, 0):
-        assert lib.exattn_set_variant(0, v) == 0
-    assert lib.exattn_set_variant(0, 3) == 4
-    p = _problem()
-    ws = {}
-    for v in (1, 2, 0):
-        assert lib.exattn_set_variant(1, v) == 0
-        ws[v] = lib.exattn_bwd_workspace_size(ctypes.byref(p))
+@pytest.mark.parametrize("kw", [dict(o_stride=(0, 1 << 23, 128)), dict(do_stride=(0, 1 << 24, 128))])
+def test_backward_only_strides_rejected(lib, kw):
+    """out and dout strides exist only for the backward: it rejects them before any launch."""
+    p = _problem(**kw)
+    assert lib.exattn_bwd(ctypes.byref(p), *([16] * 9), 256, 1 << 30, None) == 5
+    assert lib.exattn_bwd_workspace_size(ctypes.byref(p)) == 0
+
+
+def test_token_stride_limit_boundary(lib):
+    """The largest accepted token stride is 2^23 - 8 elements (a multiple of 8)."""
+    big = (1 << 23) - 8
+    assert lib.exattn_check(ctypes.byref(_problem(q_stride=(0, big, 128)))) == 0
+    assert lib.exattn_check(ctypes.byref(_problem(k_stride=(0, big, 128)))) == 0
+
+
+def test_variant_is_per_call(lib):
+    """Each problem carries its own tiling selection, so the workspace size of one call
+    never depends on another thread's choice."""
+    ws = {v: lib.exattn_bwd_workspace_size(ctypes.byref(_problem(bwd_variant=v))) for v in (0, 1, 2)}
     # the fused variant also needs the fp32 dQ accumulator [rows_q, H, D]
     assert ws[1] >= ws[0] + 2 * 100 * 4 * 128 * 4
     # the two split variants share the workspace layout
     assert ws[2] == ws[0]
-    assert lib.exattn_set_variant(1, 3) == 4
-    assert lib.exattn_set_variant(7, 0) == 4
+    # fp16 runs the split backward for every variant
+    assert lib.exattn_bwd_workspace_size(ctypes.byref(_problem(dtype=1, bwd_variant=1))) == ws[0]
+    for v in (0, 1, 2):
+        assert lib.exattn_check(ctypes.byref(_problem(fwd_variant=v))) == 0
+    # the fp8 forward has one tiling
+    assert lib.exattn_check(ctypes.byref(_problem(dtype=2, fwd_variant=1))) == 4
+    assert not hasattr(lib, "exattn_set_variant")
+
+
+def test_host_cu_seqlens_checks():
+    """Host offsets are checked by the binding before anything reaches the library: start
+    at 0, non-decreasing, end within the packed rows, and a given max_seqlen may not be
+    below the longest sequence (its rows past max_seqlen would not be computed)."""
+    from exact_attention_40_amd import api
+    assert api._host_cu_longest([0, 3, 3, 10], 10, "cu_seqlens_q", None) == 7
+    assert api._host_cu_longest([0, 3, 3, 10], 12, "cu_seqlens_q", 9) == 7
+    for c, total, given in (([1, 3], 5, None), ([0, 4, 3], 5, None), ([0, 6], 5, None),
+                            ([0, 3, 10], 10, 6)):
+        with pytest.raises(ValueError):
+            api._host_cu_longest(c, total, "cu_seqlens_q", given)
