@@ -31,45 +31,69 @@
 namespace exattn {
 
 // ----------------------------------------------------------------------------------------
-// 1. Delta / lse2 / dQ-accumulator clear. One group of D/8 lanes per (row, head).
+// 1. Delta / lse2 / dQ-accumulator clear. One block = 64 consecutive rows (tokens) of one
+// head; D/8 lanes per row read that row's O and dO once (whole 2*D-byte rows), and the 64
+// row results are stored together, so Delta and lse2 go out as whole contiguous runs (a
+// dense run may straddle two batch entries).
 // ----------------------------------------------------------------------------------------
+constexpr int kDeltaRows = 64;
+
 template <class E, int D, bool VARLEN>
 __global__ void __launch_bounds__(256) delta_kernel(BwdArgs a) {
   using V8 = typename Ty<E>::v8;
   constexpr int LPR = D / 8;            // lanes per row
-  constexpr int RPB = 256 / LPR;        // rows per block
+  constexpr int RPP = 256 / LPR;        // rows per pass
+  __shared__ float part[kDeltaRows];
+  const int head = (int)(blockIdx.x % a.H);
+  const int64_t tok0 = (int64_t)(blockIdx.x / a.H) * kDeltaRows;
   const int sub = threadIdx.x % LPR;
-  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int64_t nrows = (int64_t)a.rows_q * a.H;
-  if (r >= nrows) return;
-  const int tok = (int)(r / a.H), head = (int)(r % a.H);
-  int64_t o_off, do_off, st_idx;
-  if constexpr (VARLEN) {
-    o_off = (int64_t)tok * a.o_ss + (int64_t)head * a.o_sh;
-    do_off = (int64_t)tok * a.do_ss + (int64_t)head * a.do_sh;
-    st_idx = (int64_t)head * a.lse_row + tok;
-  } else {
-    const int b = tok / a.Sq, s = tok % a.Sq;
-    o_off = (int64_t)b * a.o_sb + (int64_t)s * a.o_ss + (int64_t)head * a.o_sh;
-    do_off = (int64_t)b * a.do_sb + (int64_t)s * a.do_ss + (int64_t)head * a.do_sh;
-    st_idx = ((int64_t)b * a.H + head) * a.Sq + s;
-  }
-  const V8 o = *reinterpret_cast<const V8*>(reinterpret_cast<const E*>(a.out) + o_off + sub * 8);
-  const V8 g = *reinterpret_cast<const V8*>(reinterpret_cast<const E*>(a.dout) + do_off + sub * 8);
-  float acc = 0.f;
+  // row index of token `tok` in the lse layout
+  auto st_index = [&](int64_t tok) -> int64_t {
+    if constexpr (VARLEN) {
+      return (int64_t)head * a.lse_row + tok;
+    } else {
+      const int64_t b = tok / a.Sq, s = tok % a.Sq;
+      return (b * a.H + head) * a.Sq + s;
+    }
+  };
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc += (float)o[i] * (float)g[i];
+  for (int pass = 0; pass < kDeltaRows / RPP; ++pass) {
+    const int lr = pass * RPP + (int)threadIdx.x / LPR;
+    const int64_t tok = tok0 + lr;
+    float acc = 0.f;
+    if (tok < a.rows_q) {
+      int64_t o_off, do_off;
+      if constexpr (VARLEN) {
+        o_off = tok * a.o_ss + (int64_t)head * a.o_sh;
+        do_off = tok * a.do_ss + (int64_t)head * a.do_sh;
+      } else {
+        const int64_t b = tok / a.Sq, s = tok % a.Sq;
+        o_off = b * a.o_sb + s * a.o_ss + (int64_t)head * a.o_sh;
+        do_off = b * a.do_sb + s * a.do_ss + (int64_t)head * a.do_sh;
+      }
+      const V8 o = *reinterpret_cast<const V8*>(reinterpret_cast<const E*>(a.out) + o_off + sub * 8);
+      const V8 g = *reinterpret_cast<const V8*>(reinterpret_cast<const E*>(a.dout) + do_off + sub * 8);
 #pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (a.dq_acc != nullptr) {
-    float* dqa = a.dq_acc + r * D + sub * 8;
-    reinterpret_cast<f32x4*>(dqa)[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    reinterpret_cast<f32x4*>(dqa)[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 8; ++i) acc += (float)o[i] * (float)g[i];
+      if (a.dq_acc != nullptr) {
+        float* dqa = a.dq_acc + (tok * a.H + head) * D + sub * 8;
+        reinterpret_cast<f32x4*>(dqa)[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        reinterpret_cast<f32x4*>(dqa)[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (sub == 0) part[lr] = acc;
   }
-  if (sub == 0) {
-    const float l = a.lse[st_idx];
-    a.delta[st_idx] = acc;
-    a.lse2[st_idx] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+  __syncthreads();
+  if (threadIdx.x < kDeltaRows) {
+    const int64_t tok = tok0 + threadIdx.x;
+    if (tok < a.rows_q) {
+      const int64_t st = st_index(tok);
+      const float l = a.lse[st];
+      a.delta[st] = part[threadIdx.x];
+      a.lse2[st] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+    }
   }
 }
 
@@ -180,9 +204,11 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
   int Sq, Sk;
   int64_t qrow0, krow0, qb_off, kb_off, vb_off, dob_off, st_unit;
   if constexpr (VARLEN) {
-    const int qs = a.cu_q[unit], ks = a.cu_k[unit];
-    Sq = a.cu_q[unit + 1] - qs;
-    Sk = a.cu_k[unit + 1] - ks;
+    const SeqRows rq = seq_rows(a.cu_q, unit, a.Sq, a.max_sq);
+    const SeqRows rk = seq_rows(a.cu_k, unit, a.Sk, a.max_sk);
+    const int qs = rq.beg, ks = rk.beg;
+    Sq = rq.len;
+    Sk = rk.len;
     qrow0 = qs;
     krow0 = ks;
     qb_off = (int64_t)qs * a.q_ss;
@@ -368,7 +394,7 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
               } else {
                 const float bias = (float)mask_bf[mi];
                 vis = vis && (bias != -INFINITY);
-                b2 = vis ? bias * kLog2e : 0.f;
+                b2 = vis ? bias_log2(bias) : 0.f;
               }
             }
             const float e2 = fast_exp2(min0(fmaf(s[r], c2, b2 - l2[e])));
@@ -494,22 +520,15 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
   }
   if (it < n_iter) iteration(it, std::integral_constant<int, 0>{});
 
-  // Epilogue: dV (wave A) or dK times scale (wave B) as bf16 into contiguous
-  // [rows_k, Hkv, D]; rows past the sequence end are dropped by the buffer range.
+  // Epilogue: dV (wave A) or dK times scale (wave B) in the input format into contiguous
+  // [rows_k, Hkv, D], whole rows staged through this wave's slice of LDS (free after the
+  // last barrier); rows past the sequence end are not written.
+  __syncthreads();
+  static_assert(T::NW * 32 * D * 2 <= bwd_smem_bytes<D, DQ>(), "epilogue staging fits the LDS");
   const float sc = role_a ? 1.f : a.scale;
-  const int64_t kv_off = ((krow0 + kb0) * a.Hkv + g) * D;
-  const uint32_t kv_bytes = (uint32_t)((krows - 1) * a.Hkv * D + D) * 2u;
-  const auto rout = make_rsrc(reinterpret_cast<E*>(role_a ? a.dv : a.dk) + kv_off, kv_bytes);
-#pragma unroll
-  for (int db = 0; db < T::DB; ++db) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kg * 32 + acc_row(r, half);
-      const int off = (key * a.Hkv * D + db * 32 + l32) * 2;
-      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (E)(acc[db][r] * sc)),
-                                            rout, off, 0, 0);
-    }
-  }
+  E* dst = reinterpret_cast<E*>(role_a ? a.dv : a.dk) + ((krow0 + kb0 + kg * 32) * a.Hkv + g) * D;
+  wave_store_cols<D, E>(smem + wave * 32 * D * 2, acc, sc, dst, (int64_t)a.Hkv * D,
+                        krows - kg * 32, lane);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -575,9 +594,11 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
   int Sq, Sk;
   int64_t qrow0, q_base, k_base, v_base, do_base, st_base, m_base = 0;
   if constexpr (VARLEN) {
-    const int qs = a.cu_q[unit], ks = a.cu_k[unit];
-    Sq = a.cu_q[unit + 1] - qs;
-    Sk = a.cu_k[unit + 1] - ks;
+    const SeqRows rq = seq_rows(a.cu_q, unit, a.Sq, a.max_sq);
+    const SeqRows rk = seq_rows(a.cu_k, unit, a.Sk, a.max_sk);
+    const int qs = rq.beg, ks = rk.beg;
+    Sq = rq.len;
+    Sk = rk.len;
     qrow0 = qs;
     q_base = (int64_t)qs * a.q_ss + (int64_t)head * a.q_sh;
     do_base = (int64_t)qs * a.do_ss + (int64_t)head * a.do_sh;
@@ -701,7 +722,7 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
           } else {
             const float bias = (float)mask_bf[mi];
             vis = vis && (bias != -INFINITY);
-            b2 = vis ? bias * kLog2e : 0.f;
+            b2 = vis ? bias_log2(bias) : 0.f;
           }
         }
         const float e2 = fast_exp2(min0(fmaf(s[kb][r], c2, b2 - l2)));
@@ -831,36 +852,41 @@ __global__ void __launch_bounds__(256) dq_reduce_kernel(BwdArgs a, int64_t n8) {
 }
 
 // ----------------------------------------------------------------------------------------
-// 4. Packed layouts: key rows past cu_seqlens_k[num_seqs] get dk = dv = 0.
+// 4. Packed layouts: key rows that no sequence computes (past cu_seqlens_k[num_seqs], or
+// past max_seqlen_k rows of their sequence) get dk = dv = 0.
 // ----------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) kv_tail_kernel(BwdArgs a, int64_t row_chunks, int chunks_per_row) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= row_chunks) return;
-  const int64_t row = i / chunks_per_row;
-  if (row < a.cu_k[a.num_units]) return;
+  const int row = (int)(i / chunks_per_row);
+  if (!row_uncovered(a.cu_k, a.num_units, row, a.Sk, a.max_sk)) return;
   reinterpret_cast<u32x4*>(a.dk)[i] = u32x4{0, 0, 0, 0};
   reinterpret_cast<u32x4*>(a.dv)[i] = u32x4{0, 0, 0, 0};
 }
 
-// Packed layouts, deterministic dQ: query rows past cu_seqlens_q[num_seqs] get dq = 0.
+// Packed layouts, deterministic dQ: query rows that no sequence computes get dq = 0.
 __global__ void __launch_bounds__(256) q_tail_kernel(BwdArgs a, int64_t row_chunks, int chunks_per_row) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= row_chunks) return;
-  const int64_t row = i / chunks_per_row;
-  if (row < a.cu_q[a.num_units]) return;
+  const int row = (int)(i / chunks_per_row);
+  if (!row_uncovered(a.cu_q, a.num_units, row, a.Sq, a.max_sq)) return;
   reinterpret_cast<u32x4*>(a.dq)[i] = u32x4{0, 0, 0, 0};
 }
 
-// Packed layouts: order[rank] = sequence, ranked by q_len * k_len (largest first, ties by
-// index). The ranks form a permutation, so every slot is written exactly once.
-__global__ void __launch_bounds__(256) unit_order_kernel(const int32_t* cu_q, const int32_t* cu_k,
-                                                         int n, int32_t* order) {
+// Packed layouts: order[rank] = sequence, ranked by q_len * k_len of the clamped, truncated
+// sequences (largest first, ties by index). The ranks form a permutation, so every slot is
+// written exactly once.
+__global__ void __launch_bounds__(256) unit_order_kernel(BwdArgs a, int32_t* order) {
+  const int n = a.num_units;
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  const int64_t wi = (int64_t)(cu_q[i + 1] - cu_q[i]) * (cu_k[i + 1] - cu_k[i]);
+  auto work = [&](int s) {
+    return (int64_t)seq_rows(a.cu_q, s, a.Sq, a.max_sq).len * seq_rows(a.cu_k, s, a.Sk, a.max_sk).len;
+  };
+  const int64_t wi = work(i);
   int rank = 0;
   for (int j = 0; j < n; ++j) {
-    const int64_t wj = (int64_t)(cu_q[j + 1] - cu_q[j]) * (cu_k[j + 1] - cu_k[j]);
+    const int64_t wj = work(j);
     rank += (wj > wi) || (wj == wi && j < i);
   }
   order[rank] = i;
@@ -888,25 +914,17 @@ hipError_t launch_unit_order(const BwdArgs& a, int32_t* order, hipStream_t s) {
   const int n = a.num_units;
   if (n <= 0) return hipSuccess;
   dim3 grid((unsigned)((n + 255) / 256)), block(256);
-  hipLaunchKernelGGL(unit_order_kernel, grid, block, 0, s, a.cu_q, a.cu_k, n, order);
+  hipLaunchKernelGGL(unit_order_kernel, grid, block, 0, s, a, order);
   return hipGetLastError();
 }
 
 int bwd_block_n(int head_dim) { return BwdTile<128>::BN; }
 
-// Backward variants: 0 = pipelined dK/dV kernel (bwd_kv.hip) + separate dQ kernel
-// (deterministic), 1 = one fused kernel with fp32 dQ atomics, 2 = the two-barrier dK/dV
-// kernel above + the same dQ kernel.
-static int g_bwd_variant = 0;
-void set_bwd_variant(int v) { g_bwd_variant = (v == 1 || v == 2) ? v : 0; }
-int get_bwd_variant() { return g_bwd_variant; }
-
 template <class E>
 static hipError_t launch_delta_e(const BwdArgs& a, int head_dim, bool varlen, hipStream_t s) {
-  const int64_t nrows = (int64_t)a.rows_q * a.H;
-  if (nrows <= 0) return hipSuccess;
-  const int rpb = 256 / (head_dim / 8);
-  dim3 grid((unsigned)((nrows + rpb - 1) / rpb)), block(256);
+  const int64_t nblk = ((int64_t)a.rows_q + kDeltaRows - 1) / kDeltaRows * a.H;
+  if (nblk <= 0) return hipSuccess;
+  dim3 grid((unsigned)nblk), block(256);
   if (head_dim == 64) {
     if (varlen) hipLaunchKernelGGL((delta_kernel<E, 64, true>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((delta_kernel<E, 64, false>), grid, block, 0, s, a);

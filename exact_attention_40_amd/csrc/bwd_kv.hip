@@ -93,9 +93,11 @@ __global__ void __launch_bounds__(512) bwd_kv_kernel(BwdArgs a) {
   int Sq, Sk;
   int64_t krow0, qb_off, kb_off, vb_off, dob_off, st_unit;
   if constexpr (VARLEN) {
-    const int qs = a.cu_q[unit], ks = a.cu_k[unit];
-    Sq = a.cu_q[unit + 1] - qs;
-    Sk = a.cu_k[unit + 1] - ks;
+    const SeqRows rq = seq_rows(a.cu_q, unit, a.Sq, a.max_sq);
+    const SeqRows rk = seq_rows(a.cu_k, unit, a.Sk, a.max_sk);
+    const int qs = rq.beg, ks = rk.beg;
+    Sq = rq.len;
+    Sk = rk.len;
     krow0 = ks;
     qb_off = (int64_t)qs * a.q_ss;
     kb_off = (int64_t)ks * a.k_ss;
@@ -269,7 +271,7 @@ __global__ void __launch_bounds__(512) bwd_kv_kernel(BwdArgs a) {
         } else {
           const float bias = (float)mask_bf[mi];
           vis = vis && (bias != -INFINITY);
-          b2 = vis ? bias * kLog2e : 0.f;
+          b2 = vis ? bias_log2(bias) : 0.f;
         }
         const float e2 = fast_exp2(min0(fmaf(sp[qb][r], c2, b2 - lv)));
         sp[qb][r] = vis ? e2 : 0.f;
@@ -450,23 +452,15 @@ __global__ void __launch_bounds__(512) bwd_kv_kernel(BwdArgs a) {
     });
   }
 
-  // Epilogue: dV (wave A) or dK times scale (wave B) as bf16 into contiguous
-  // [rows_k, Hkv, D]; rows past the sequence end are dropped by the buffer range. Keys
-  // that no query sees are written as exact zeros.
+  // Epilogue: dV (wave A) or dK times scale (wave B) in the input format into contiguous
+  // [rows_k, Hkv, D], staged through this wave's slice of LDS (every wave has passed the
+  // last barrier) so that whole rows are stored; rows past the sequence end are not
+  // written. Keys that no query sees are written as exact zeros.
+  static_assert(T::NW * 32 * D * 2 <= T::SMEM, "epilogue staging fits the LDS");
   const float sc = role_a ? 1.f : a.scale;
-  const int64_t kv_off = ((krow0 + kb0) * a.Hkv + g) * D;
-  const uint32_t kv_bytes = (uint32_t)((krows - 1) * a.Hkv * D + D) * 2u;
-  const auto rout = make_rsrc(reinterpret_cast<E*>(role_a ? a.dv : a.dk) + kv_off, kv_bytes);
-#pragma unroll
-  for (int db = 0; db < T::DB; ++db) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kg * 32 + acc_row(r, half);
-      const int off = (key * a.Hkv * D + db * 32 + l32) * 2;
-      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (E)(acc[db][r] * sc)),
-                                            rout, off, 0, 0);
-    }
-  }
+  E* dst = reinterpret_cast<E*>(role_a ? a.dv : a.dk) + ((krow0 + kb0 + kg * 32) * a.Hkv + g) * D;
+  wave_store_cols<D, E>(smem + wave * 32 * D * 2, acc, sc, dst, (int64_t)a.Hkv * D,
+                        krows - kg * 32, lane);
 }
 
 template <class E, int D>

@@ -56,6 +56,16 @@ __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// An additive mask value in log2 units, bias * log2(e), rounded once. The product must not
+// be contracted into a later add (hipcc fuses across statements by default): the row max
+// and the exponent must see the same rounded value, or the exponent picks up the product's
+// rounding error, about |bias| * 2^-24, which overflows exp2 for a huge finite bias such as
+// -1e30.
+__device__ __forceinline__ float bias_log2(float bias) {
+#pragma clang fp contract(off)
+  return bias * kLog2e;
+}
+
 // min(x, 0) that keeps NaN (v_minimum3_f32): the backward's exponent clamp must not turn a
 // NaN score or lse into exp2(0) = 1.
 __device__ __forceinline__ float min0(float x) { return __builtin_elementwise_minimum(x, 0.f); }
@@ -109,6 +119,37 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 }
 
 __device__ __forceinline__ float wave_xor32(float v) { return __shfl_xor(v, 32, 64); }
+
+// Rows of packed sequence s: [beg, beg + len). The caller's device offsets are trusted only
+// as far as they stay inside the packed tensor: each is clamped into [0, total], the end is
+// at least the start, and the length is cut to `cap` (max_seqlen: the grid covers that
+// many rows per sequence). So no offset array makes a kernel touch rows outside [0, total).
+struct SeqRows {
+  int beg, len;
+};
+__device__ __forceinline__ int clamp_cu(const int32_t* cu, int i, int total) {
+  return min(max(cu[i], 0), total);
+}
+__device__ __forceinline__ SeqRows seq_rows(const int32_t* cu, int s, int total, int cap) {
+  const int b = clamp_cu(cu, s, total);
+  const int e = max(clamp_cu(cu, s + 1, total), b);
+  return {b, min(e - b, cap)};
+}
+
+// Whether packed row r (0 <= r < total) is outside the rows the kernels compute: before the
+// first or past the last sequence, or past the first `cap` rows of its own sequence. The
+// sequence is found by bisection over the clamped offsets (n + 1 entries).
+__device__ __forceinline__ bool row_uncovered(const int32_t* cu, int n, int r, int total, int cap) {
+  if (r < clamp_cu(cu, 0, total) || r >= clamp_cu(cu, n, total)) return true;
+  int lo = 0, hi = n;   // invariant for sorted offsets: cu[lo] <= r < cu[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (clamp_cu(cu, mid, total) <= r) lo = mid;
+    else hi = mid;
+  }
+  const SeqRows sr = seq_rows(cu, lo, total, cap);
+  return r - sr.beg >= sr.len;
+}
 
 // max and sum of the values held by lanes l and l ^ 32, on both lanes, in one
 // v_permlane32_swap (which exchanges the upper half of one register with the lower half of
@@ -250,6 +291,41 @@ __device__ __forceinline__ void wave_store_rows(unsigned char* buf, const f32x16
                  acc[db][4 * rg + 3] * scale};
       *reinterpret_cast<V4*>(buf + l32 * RB + 16 * ((c8 >> 1) ^ (l32 & (CPR - 1))) + 8 * (c8 & 1)) =
           __builtin_convertvector(v, V4);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int RPI = 64 / CPR;                  // rows per instruction
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CPR, c = lane % CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(buf + r * RB + 16 * (c ^ (r & (CPR - 1))));
+    if (r < nrows) *reinterpret_cast<u32x4*>(dst + (int64_t)r * row_stride + 8 * c) = v;
+  }
+}
+
+// Store a wave's 32 x D result block as rows of the input format, coalesced, for an
+// accumulator in the other orientation: lane = column, `acc[db]` register r = row
+// acc_row(r, l / 32), column db*32 + l % 32. Each value goes to this wave's own 32 * D * 2
+// bytes of LDS `buf` (16-byte chunks XOR-swizzled by the row's low bits), then each lane
+// stores 16 contiguous bytes, so every store instruction covers whole rows. Rows
+// r >= nrows are not written. The caller makes sure no other wave uses `buf` meanwhile.
+template <int D, class E>
+__device__ __forceinline__ void wave_store_cols(unsigned char* buf, const f32x16 (&acc)[D / 32],
+                                                float scale, E* dst, int64_t row_stride,
+                                                int nrows, int lane) {
+  constexpr int RB = D * 2;
+  constexpr int CPR = D / 8;
+  const int half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int col = db * 32 + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = acc_row(r, half);
+      *reinterpret_cast<E*>(buf + row * RB + 16 * ((col >> 3) ^ (row & (CPR - 1))) + 2 * (col & 7)) =
+          (E)(acc[db][r] * scale);
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -104,9 +104,11 @@ fwd_kernel(FwdArgs a) {
   int Sq, Sk;
   int64_t q_base, k_base, v_base, o_base, lse_base, m_base = 0;
   if constexpr (VARLEN) {
-    const int qs = a.cu_q[unit], ks = a.cu_k[unit];
-    Sq = a.cu_q[unit + 1] - qs;
-    Sk = a.cu_k[unit + 1] - ks;
+    const SeqRows rq = seq_rows(a.cu_q, unit, a.Sq, a.max_sq);
+    const SeqRows rk = seq_rows(a.cu_k, unit, a.Sk, a.max_sk);
+    const int qs = rq.beg, ks = rk.beg;
+    Sq = rq.len;
+    Sk = rk.len;
     q_base = (int64_t)qs * a.q_ss + (int64_t)head * a.q_sh;
     k_base = (int64_t)ks * a.k_ss + (int64_t)g * a.k_sh;
     v_base = (int64_t)ks * a.v_ss + (int64_t)g * a.v_sh;
@@ -219,7 +221,7 @@ fwd_kernel(FwdArgs a) {
       } else {
         const float bias = (float)mask_bf[mi];
         vis = vis && (bias != -INFINITY);
-        b2 = vis ? bias * kLog2e : 0.f;
+        b2 = vis ? bias_log2(bias) : 0.f;
       }
     }
     return vis;
@@ -500,13 +502,14 @@ fwd_kernel(FwdArgs a) {
   }
 }
 
-// Rows of a packed output past cu_seqlens_q[num_seqs]: out = 0, lse = -inf.
+// Rows of a packed output that no sequence computes (past cu_seqlens_q[num_seqs], or past
+// max_seqlen_q rows of their sequence): out = 0, lse = -inf.
 template <int D>
 __global__ void __launch_bounds__(256) fwd_tail_kernel(FwdArgs a) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)a.Sq * a.H) return;
   const int row = (int)(idx / a.H), head = (int)(idx % a.H);
-  if (row < a.cu_q[a.num_units]) return;
+  if (!row_uncovered(a.cu_q, a.num_units, row, a.Sq, a.max_sq)) return;
   uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (int64_t)row * a.o_ss + (int64_t)head * a.o_sh;
 #pragma unroll
   for (int d = 0; d < D; d += 8) *reinterpret_cast<u32x4*>(o + d) = u32x4{0, 0, 0, 0};
@@ -516,15 +519,9 @@ __global__ void __launch_bounds__(256) fwd_tail_kernel(FwdArgs a) {
 // Variants: 0 = 8 waves x 32 rows, lazy rescale (default); 1 = 8 waves x 32 rows, eager
 // rescale; 2 = 4 waves x 64 rows (lazy), one wave per SIMD. Variant 2 is compiled for bf16,
 // head_dim 128, without a mask or cu_seqlens; other problems use variant 0.
-static int g_fwd_variant = 0;
-
-void set_fwd_variant(int v) { g_fwd_variant = (v >= 0 && v <= 2) ? v : 0; }
-int get_fwd_variant() { return g_fwd_variant; }
-
-static int effective_variant(int head_dim, int dtype, int mask, bool varlen) {
-  const int v = g_fwd_variant;
+static int effective_variant(int v, int head_dim, int dtype, int mask, bool varlen) {
   if (v == 2 && (head_dim != 128 || dtype != kDtypeBf16 || mask != kMaskNone || varlen)) return 0;
-  return v;
+  return (v >= 0 && v <= 2) ? v : 0;
 }
 
 int fwd_block_m(int head_dim, int mask, bool varlen) { return 256; }
@@ -582,8 +579,8 @@ static hipError_t launch_fwd_e(const FwdArgs& a, int head_dim, int v, bool causa
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, int dtype, bool causal, int mask,
-                      bool varlen, hipStream_t s) {
-  const int v = effective_variant(head_dim, dtype, mask, varlen);
+                      bool varlen, int variant, hipStream_t s) {
+  const int v = effective_variant(variant, head_dim, dtype, mask, varlen);
   if (v == 2) return launch_fwd_plain128<4, 2>(a, causal, s);
   if (dtype == kDtypeF16) return launch_fwd_e<f16>(a, head_dim, v, causal, mask, varlen, s);
   return launch_fwd_e<bf16>(a, head_dim, v, causal, mask, varlen, s);
