@@ -21,6 +21,11 @@ Workloads (the pages describe the shapes; every value here is synthetic):
 * ``varlen_gqa`` - 16 packed sequences with lengths uniform in [128, 4096], H32 Hkv8, causal.
 * ``long_causal`` - B1 S61380 H32 D128 causal (FlyDSL PR #1033, "Result": the shortest
   sequence length of its throughput table).
+* ``masked`` - dense inputs with a bool mask or an additive bf16 bias in a chosen shape
+  (per-head [B, H, S_q, S_k], per-batch [B, 1, S_q, S_k] or 2-D [S_q, S_k]): OpenWAM PR #64
+  ("Fix") reads an additive mask's -inf as hidden and a finite value as a bias added to
+  the score. Biases are N(0,1) * bias_std rounded to bf16, with a fraction of -inf entries;
+  optional rows hold one constant bias for every key (a constant cancels in the softmax).
 * ``fp8_dense`` - fp8 e4m3 q, k, v with one descale per tensor for the fp8 forward
   (FlyDSL PR #1033, "The fp8 helper, second commit": K scaled by a large factor, V = ones
   in some of its runs). ``kind="normal"`` quantises N(0,1) draws (the descale maps the
@@ -38,7 +43,7 @@ import numpy as np
 import torch
 
 __all__ = ["Problem", "Fp8Problem", "fp8_dense", "dense", "dv_nan_repro", "padded_tile", "wide_logit", "varlen_gqa",
-           "long_causal", "PADDED_TILE_SHAPES", "WIDE_LOGIT_SCALES"]
+           "long_causal", "masked", "PADDED_TILE_SHAPES", "WIDE_LOGIT_SCALES"]
 
 PADDED_TILE_SHAPES = ((392, 392), (360, 64), (100, 77))
 WIDE_LOGIT_SCALES = (1, 8, 16, 24, 32, 48, 64)
@@ -161,6 +166,39 @@ def padded_tile(sq, sk, mask_kind="bool", seed=2000, D=128, B=2, H=4, anti_row=T
     return Problem(f"padded_tile_{sq}x{sk}_{mask_kind}", bf(q32), bf(k32), bf(v32), bf(do32),
                    causal=False, mask=mask, mask_kind=kind,
                    meta=dict(B=B, Sq=sq, Sk=sk, H=H, Hkv=H, D=D, seed=seed, anti_rows=rows))
+
+
+def masked(B, Sq, Sk, H, Hkv, D, seed, *, kind="additive", shape="per_head", causal=False,
+           bias_std=4.0, hide_frac=0.1, const_rows=(), dtype=torch.bfloat16):
+    """Dense inputs (q, k, v, dout ~ N(0,1)) with a mask of `shape` "per_head"
+    [B, H, Sq, Sk], "per_batch" [B, 1, Sq, Sk] or "2d" [Sq, Sk].
+
+    kind "additive": bf16 bias N(0,1) * bias_std, with about `hide_frac` of the entries -inf
+    (key 0 of every row stays finite). kind "bool": True = attend with probability
+    1 - hide_frac (key 0 always kept). ``const_rows`` is a list of ((b, h, i), value): that
+    row of the bias holds `value` for every key (additive, per-head shape only).
+    """
+    p = dense(B, Sq, Sk, H, Hkv, D, seed, causal=causal, name=f"masked_{kind}_{shape}",
+              dtype=dtype)
+    rng = _rng(seed + 500)
+    full = {"per_head": (B, H, Sq, Sk), "per_batch": (B, 1, Sq, Sk), "2d": (Sq, Sk)}[shape]
+    hide = rng.random(size=full) < hide_frac
+    hide[..., 0] = False
+    if kind == "bool":
+        mask = torch.from_numpy(~hide)
+    elif kind == "additive":
+        bias = rng.standard_normal(size=full).astype(np.float32) * np.float32(bias_std)
+        bias[hide] = -np.inf
+        for (b, h, i), value in const_rows:
+            if shape != "per_head":
+                raise ValueError("constant rows need the per-head shape")
+            bias[b, h, i, :] = np.float32(value)
+        mask = torch.from_numpy(bias).to(torch.bfloat16)
+    else:
+        raise ValueError(kind)
+    p.mask, p.mask_kind = mask, ("bool" if kind == "bool" else "additive")
+    p.meta.update(mask_shape=shape, const_rows=list(const_rows))
+    return p
 
 
 def wide_logit(s, seed=None, B=2, S=8192, H=32, D=128, dtype=torch.bfloat16):

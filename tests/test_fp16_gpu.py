@@ -51,11 +51,7 @@ def test_fp16_ignores_fused_variant():
     """Backward variant 1 (bf16 atomics) leaves fp16 on the split path: same bits."""
     p = CASES[0]["make"]()
     base = run_gpu(p)
-    try:
-        api.set_variant(1, 1)
-        other = run_gpu(p)
-    finally:
-        api.set_variant(1, 0)
+    other = run_gpu(p, bwd_variant=1)
     for n in ("out", "lse", "dq", "dk", "dv"):
         assert torch.equal(base[n], other[n]), n
     say("fp16 fused-variant fallback ok")

@@ -1,12 +1,15 @@
 """Parity of the HIP path (called through the C ABI) against the float64 oracle.
 
-Bars: rel-L2 <= 1e-2 for out and lse, <= 2e-2 for dq, dk and dv, zero non-finite values,
-exact empty-row sentinels. Element-by-element at sizes spanning several tiles with ragged
-tails; at the full workload sizes on sampled units, rows and keys plus invariants that hold
-at any size.
+Bars: rel-L2 <= 1e-2 for out and lse, <= 2e-2 for dq, dk and dv, over each whole tensor and
+over every single row (``gpu_util.compare``), zero non-finite values, exact empty-row
+sentinels. Whole tensors at sizes spanning several tiles with ragged tails; at the full
+workload sizes on sampled units, rows and keys plus invariants that hold at any size. The
+pages' own accuracy figures are asserted as upper bounds where the workload is theirs.
 """
 
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -14,9 +17,12 @@ import torch
 
 import oracle
 from exact_attention_40_amd import api, workloads
-from gpu_util import compare, f64, nonfinite, run_gpu, run_oracle, say
+from gpu_util import compare, f64, nonfinite, rel_l2, run_gpu, run_oracle, say
 
 pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "page_values.json")
+PAGE = json.load(open(GOLDEN))
 
 
 # ------------------------------------------------------------------------------------------
@@ -77,9 +83,21 @@ def test_padded_tile_low_lse_row(shape, kind, layout):
     assert nonfinite(g["dq"]) == 0 and nonfinite(g["dk"]) == 0 and nonfinite(g["dv"]) == 0
     ref = run_oracle(p)
     compare(g, ref, tag=f"{p.name}_{layout}")
+    # the anti-aligned rows on their own: the page's bug sits in exactly these rows
     for b, r in p.meta["anti_rows"].items():
         lse_row = f64(g["lse"])[b, :, r]
         assert np.all(lse_row < -100), lse_row
+        errs = dict(out=rel_l2(f64(g["out"])[b, r], ref["out"][b, r]),
+                    lse=rel_l2(lse_row, ref["lse"][b, :, r]),
+                    dq=rel_l2(f64(g["dq"])[b, r], ref["dq"][b, r]))
+        say(f"  anti-aligned row b={b} r={r}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+        for n, e in errs.items():
+            assert e <= {"out": 1e-2, "lse": 1e-2, "dq": 2e-2}[n], (b, r, n, e)
+    # OpenWAM PR #64, "Validation": after the fix the forward is within 0.016 of the fp32
+    # reference in max abs and the gradients within 1%; held here against the float64 oracle
+    assert float(np.max(np.abs(f64(g["out"]) - ref["out"]))) <= 0.016
+    for n in ("dq", "dk", "dv"):
+        assert rel_l2(f64(g[n]), ref[n]) <= 1e-2, n
     if kind == "keypad":
         Sk = shape[1]
         Lb = math.ceil(0.75 * Sk)
@@ -121,20 +139,26 @@ def _unit_slices(p, b, g):
 @pytest.mark.parametrize("s", workloads.WIDE_LOGIT_SCALES)
 def test_wide_logit_full_size(s):
     """B2 S8192 H32 D128 at every k scale: zero non-finite values everywhere; one full
-    (batch, head) unit compared element by element with the oracle at s in {1, 32, 64}."""
+    (batch, head) unit compared with the oracle, forward and backward, row by row. At the
+    scales FlyDSL PR #1033 tabulates ("Result": forward rel-L2 against fp32 after the fix),
+    that unit's out must also be no worse than the page's figure."""
     p = workloads.wide_logit(s)
     g = run_gpu(p)
     for n in ("out", "lse", "dq", "dk", "dv"):
         assert nonfinite(g[n]) == 0, n
-    if s in (1, 32, 64):
-        b, h = 1, 5
-        sub, hs = _unit_slices(p, b, h)
-        ref = run_oracle(sub)
-        sel = {n: (slice(b, b + 1), slice(None), hs) for n in ("out", "dq")}
-        sel["lse"] = (slice(b, b + 1), hs)
-        sel.update({n: (slice(b, b + 1), slice(None), slice(h, h + 1)) for n in ("dk", "dv")})
-        gs = {n: g[n][sel[n]] for n in sel}
-        compare(gs, ref, tag=f"{p.name} unit(b={b},h={h})")
+    b, h = 1, 5
+    sub, hs = _unit_slices(p, b, h)
+    ref = run_oracle(sub)
+    sel = {n: (slice(b, b + 1), slice(None), hs) for n in ("out", "dq")}
+    sel["lse"] = (slice(b, b + 1), hs)
+    sel.update({n: (slice(b, b + 1), slice(None), slice(h, h + 1)) for n in ("dk", "dv")})
+    gs = {n: g[n][sel[n]] for n in sel}
+    rep = compare(gs, ref, tag=f"{p.name} unit(b={b},h={h})")
+    page = PAGE["fwd_rel_l2_vs_fp32_after_fix"]
+    if s in page["k_scale"]:
+        bound = page["rel_l2"][page["k_scale"].index(s)]
+        say(f"  s={s}: out rel-L2 {rep['out']:.3e}, page after the fix {bound:.3e}")
+        assert rep["out"] <= bound
 
 
 def _varlen_sub(p, s, g):
@@ -210,6 +234,65 @@ def test_varlen_many_sequences_with_ties_and_empties():
     _check_varlen(p, g, [(s, 0) for s in range(300) if lengths[s] > 0])
 
 
+def test_varlen_more_sequences_than_the_ranking():
+    """More packed sequences than the dK/dV grid ranks (8192): the backward takes the
+    unranked grid order. 9000 short sequences (lengths 0 to 40, some empty), H2 Hkv1 D64,
+    causal; a spread of sequences against the oracle and every row written."""
+    rng = np.random.default_rng(4400)
+    lengths = rng.integers(0, 41, size=9000).tolist()
+    p = workloads.varlen_gqa(seed=4401, lengths=lengths, H=2, Hkv=1, D=64, extra_rows=5)
+    g = run_gpu(p)
+    for n in ("out", "dq", "dk", "dv"):
+        assert nonfinite(g[n]) == 0, n
+    picks = [s for s in range(0, 9000, 97) if lengths[s] > 0] + [8999 if lengths[8999] else 8998]
+    _check_varlen(p, g, [(s, 0) for s in picks])
+
+
+def test_varlen_device_offsets_and_truncation():
+    """Device cu_seqlens with max_seqlen below the longest sequence: the library never
+    reads device offsets on the host, so it truncates such a sequence to max_seqlen rows
+    and keys (include/exattn.h, packed sequences) and writes the rows past it like rows past
+    the last sequence. Checked against the oracle of the truncated sequences."""
+    lengths = [300, 90, 257]
+    p = workloads.varlen_gqa(seed=4500, lengths=lengths, H=4, Hkv=2, D=128, extra_rows=11)
+    cap = 200
+    q, k, v, do, kw = __import__("gpu_util").gpu_inputs(p)
+    kw = dict(kw, cu_seqlens_q=p.cu_seqlens_q.cuda(), cu_seqlens_k=p.cu_seqlens_k.cuda(),
+              max_seqlen_q=cap, max_seqlen_k=cap)
+    junk = [torch.full((1 << 22,), float("nan"), device="cuda") for _ in range(4)]
+    del junk
+    out, lse = api.exattn_fwd(q, k, v, **kw)
+    dq, dk, dv = api.exattn_bwd(q, k, v, out, do, lse, **kw)
+    torch.cuda.synchronize()
+    g = dict(out=out, lse=lse, dq=dq, dk=dk, dv=dv)
+    for n in g:
+        assert nonfinite(g[n][~torch.isneginf(g[n])] if n == "lse" else g[n]) == 0, n
+    cu = p.cu_seqlens_q.tolist()
+    for s, L in enumerate(lengths):
+        t = min(L, cap)
+        b0 = cu[s]
+        for kvh in range(2):
+            hs = slice(2 * kvh, 2 * kvh + 2)
+            sub = workloads.Problem(f"trunc_s{s}", p.q[None, b0:b0 + t, hs], p.k[None, b0:b0 + t, kvh:kvh + 1],
+                                    p.v[None, b0:b0 + t, kvh:kvh + 1], p.dout[None, b0:b0 + t, hs],
+                                    causal=True)
+            ref = run_oracle(sub)
+            gs = dict(out=out[None, b0:b0 + t, hs], dq=dq[None, b0:b0 + t, hs],
+                      lse=lse[hs, b0:b0 + t][None], dk=dk[None, b0:b0 + t, kvh:kvh + 1],
+                      dv=dv[None, b0:b0 + t, kvh:kvh + 1])
+            compare(gs, ref, tag=sub.name)
+        # rows and keys past the truncation
+        if L > t:
+            assert torch.count_nonzero(out[b0 + t:b0 + L]) == 0
+            assert torch.isneginf(lse[:, b0 + t:b0 + L]).all()
+            for n in ("dq", "dk", "dv"):
+                assert torch.count_nonzero(g[n][b0 + t:b0 + L]) == 0, n
+    tail = cu[-1]
+    assert torch.count_nonzero(out[tail:]) == 0 and torch.isneginf(lse[:, tail:]).all()
+    for n in ("dq", "dk", "dv"):
+        assert torch.count_nonzero(g[n][tail:]) == 0, n
+
+
 def test_long_causal_sampled():
     """B1 S61380 H32 D128 causal: 64 sampled query rows (out, lse, dq), sampled keys near
     the end (dk, dv), the gradient sums over all keys, zero non-finite values."""
@@ -235,7 +318,7 @@ def test_long_causal_sampled():
         dq = oracle.rows_backward_dq(q[rr], k, v, do[rr], rr, scale, True)
         ref_o.append(o), ref_l.append(l), ref_dq.append(dq)
         got_o.append(out_g[rr, h]), got_l.append(lse_g[h, rr]), got_dq.append(dq_g[rr, h])
-    from gpu_util import rel_l2, TOL
+    from gpu_util import TOL
     eo = rel_l2(np.concatenate(got_o), np.concatenate(ref_o))
     el = rel_l2(np.concatenate(got_l), np.concatenate(ref_l))
     ed = rel_l2(np.concatenate(got_dq), np.concatenate(ref_dq))

@@ -14,14 +14,6 @@ from gpu_util import (compare, dq_reassociation_bound, dq_runs_agree, nonfinite,
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture
-def variant():
-    """Selects variants for one test and restores the defaults afterwards."""
-    yield api.set_variant
-    api.set_variant(0, 0)
-    api.set_variant(1, 0)
-
-
 FWD_CASES = [
     dict(name="dense_d128", make=lambda: workloads.dense(2, 777, 650, 4, 2, 128, seed=7001)),
     dict(name="causal_d128", make=lambda: workloads.dense(1, 900, 900, 4, 4, 128, seed=7002,
@@ -36,10 +28,9 @@ FWD_CASES = [
 
 @pytest.mark.parametrize("fwd_v", [0, 1, 2])
 @pytest.mark.parametrize("case", FWD_CASES, ids=[c["name"] for c in FWD_CASES])
-def test_forward_variants(variant, fwd_v, case):
+def test_forward_variants(fwd_v, case):
     p = case["make"]()
-    variant(0, fwd_v)
-    compare(run_gpu(p, backward=False), run_oracle(p, backward=False),
+    compare(run_gpu(p, backward=False, fwd_variant=fwd_v), run_oracle(p, backward=False),
             names=("out", "lse"), tag=f"fwd v{fwd_v} {case['name']}")
 
 
@@ -50,7 +41,7 @@ BWD_CASES = FWD_CASES + [
 
 
 @pytest.mark.parametrize("case", BWD_CASES, ids=[c["name"] for c in BWD_CASES])
-def test_fused_backward_variant(variant, case):
+def test_fused_backward_variant(case):
     """The fused backward matches the oracle, and its dq agrees with the default
     backward's within the fp32 re-association bound of its atomics (dense problems). Its
     key blocks visit the query tiles in a rotated order, so dk and dv are summed in another
@@ -58,15 +49,14 @@ def test_fused_backward_variant(variant, case):
     p = case["make"]()
     ref = run_oracle(p)
     base = run_gpu(p)
-    variant(1, 1)
-    fused = run_gpu(p)
+    fused = run_gpu(p, bwd_variant=1)
     compare(fused, ref, tag=f"bwd fused {case['name']}")
     if not p.varlen:
         assert dq_runs_agree(fused["dq"], base["dq"], dq_reassociation_bound(p))
 
 
 @pytest.mark.parametrize("s", [8, 32, 64])
-def test_lazy_rescale_not_worse_than_eager(variant, s):
+def test_lazy_rescale_not_worse_than_eager(s):
     """k scaled by s (FlyDSL PR #1033, "Repro"): both rescale policies are finite and the
     lazy one's error against the oracle is no larger than the eager one's (up to 10% and
     a small absolute slack for rounding noise)."""
@@ -74,8 +64,7 @@ def test_lazy_rescale_not_worse_than_eager(variant, s):
     ref = run_oracle(p, backward=False)
     errs = {}
     for v in (0, 1):   # 0 = lazy (default), 1 = eager
-        variant(0, v)
-        g = run_gpu(p, backward=False)
+        g = run_gpu(p, backward=False, fwd_variant=v)
         assert nonfinite(g["out"]) == 0 and nonfinite(g["lse"]) == 0
         errs[v] = compare(g, ref, names=("out", "lse"), tag=f"s={s} fwd v{v}")
     for n in ("out", "lse"):
@@ -84,7 +73,7 @@ def test_lazy_rescale_not_worse_than_eager(variant, s):
 
 
 @pytest.mark.parametrize("case", BWD_CASES, ids=[c["name"] for c in BWD_CASES])
-def test_two_barrier_backward_variant(variant, case):
+def test_two_barrier_backward_variant(case):
     """Backward variant 2 (both waves of a key group on the same query tile) matches the
     oracle; it shares the dQ kernel with the default, so dq is bitwise the same. Its dk and
     dv sum the same products in the same order as the default's pipelined kernel, which
@@ -93,8 +82,7 @@ def test_two_barrier_backward_variant(variant, case):
     p = case["make"]()
     ref = run_oracle(p)
     base = run_gpu(p)
-    variant(1, 2)
-    two = run_gpu(p)
+    two = run_gpu(p, bwd_variant=2)
     compare(two, ref, tag=f"bwd two-barrier {case['name']}")
     assert torch.equal(two["dq"], base["dq"])
     for n in ("dk", "dv"):
@@ -119,7 +107,7 @@ PHASE_CASES = [
 
 @pytest.mark.parametrize("case", PHASE_CASES, ids=lambda c: "B{}_Sq{}_Sk{}_H{}_Hkv{}_D{}_{}".format(
     *c[:6], "causal" if c[6] else "full"))
-def test_dkdv_phase_counts(variant, case):
+def test_dkdv_phase_counts(case):
     """The pipelined dK/dV kernel (default) matches the oracle and the two-barrier kernel
     (variant 2) on short tile sequences."""
     B, Sq, Sk, H, Hkv, D, causal = case
@@ -127,8 +115,7 @@ def test_dkdv_phase_counts(variant, case):
     ref = run_oracle(p)
     base = run_gpu(p)
     compare(base, ref, tag=f"phases {case}")
-    variant(1, 2)
-    two = run_gpu(p)
+    two = run_gpu(p, bwd_variant=2)
     for n in ("dk", "dv"):
         d = (two[n].double() - base[n].double()).norm() / base[n].double().norm().clamp_min(1e-30)
         assert d <= 4e-3, (n, float(d))
