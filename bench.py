@@ -61,34 +61,100 @@ def measured_traffic(kernel):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(target_seconds=15.0):
-    """The float64 oracle on a bounded sample of the same workload: whole (batch, head)
-    units of S=8192 keys, forward and backward, until about `target_seconds` elapse."""
+def _pin_blas():
+    """Worker initialiser: one BLAS thread per worker process, so the core count is exact."""
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        pass
+
+
+def _oracle_unit(seed):
+    """One whole (batch, head) unit of the benchmark workload through the float64 oracle,
+    forward and backward. Returns (FLOP, seconds)."""
+    import numpy as np  # noqa: F401
+
+    import oracle
+    from exact_attention_40_amd import workloads
+
+    p = workloads.dense(1, S, S, 1, 1, D, seed=seed)
+    q, k, v, do = (t.double().numpy() for t in (p.q, p.k, p.v, p.dout))
+    t0 = time.perf_counter()
+    oracle.attention_forward(q, k, v)
+    oracle.attention_backward(q, k, v, do)
+    return 14.0 * D * S * S, time.perf_counter() - t0
+
+
+def _oracle_long_rows():
+    """The long-sequence workload (B1 S61380 H32 D128 causal) as its GPU test samples it:
+    64 query rows through the oracle's row forward and row dQ. Returns (pairs, FLOP,
+    seconds); the FLOP count is 8*D per visible pair (forward 4*D, dP and dQ 4*D)."""
     import numpy as np
 
     import oracle
     from exact_attention_40_amd import workloads
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = 1
+    p = workloads.long_causal()
+    Sl = p.q.shape[1]
+    rng = np.random.default_rng(5001)
+    rows = np.array([0, Sl - 1, 127, 128, 61311, 61312] + sorted(rng.choice(Sl, 58, replace=False).tolist()))
+    heads = rng.integers(0, 32, size=len(rows))
+    scale = p.softmax_scale
+    pairs = 0
+    t0 = time.perf_counter()
+    for h in np.unique(heads):
+        rr = rows[heads == h]
+        q = p.q[0, :, h].double().numpy()
+        k = p.k[0, :, h].double().numpy()
+        v = p.v[0, :, h].double().numpy()
+        do = p.dout[0, :, h].double().numpy()
+        oracle.rows_forward(q[rr], k, v, rr, scale, True)
+        oracle.rows_backward_dq(q[rr], k, v, do[rr], rr, scale, True)
+        pairs += int(np.sum(rr + 1))
+    return pairs, 8.0 * D * pairs, time.perf_counter() - t0
+
+
+def cpu_baseline(max_units=64, target_seconds=10.0):
+    """The float64 oracle on a bounded sample of the benchmark workload, on the host cores:
+    one worker process per whole (batch, head) unit (S=8192 keys, forward and backward),
+    each worker's BLAS pinned to one thread, as many workers as usable cores (at most 16,
+    the host share of one GPU). Units are submitted in rounds of one per worker until about
+    `target_seconds` have passed. Also times the long-sequence workload's 64 sampled rows
+    and extrapolates, at that sample's rate, to the whole problem (labelled as such)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
+    import numpy as np
+
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
     rng = np.random.default_rng(9)
     flops = 0.0
     units = 0
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < target_seconds and units < 16:
-        p = workloads.dense(1, S, S, 1, 1, D, seed=int(rng.integers(1 << 30)))
-        q, k, v, do = (t.double().numpy() for t in (p.q, p.k, p.v, p.dout))
-        oracle.attention_forward(q, k, v)
-        oracle.attention_backward(q, k, v, do)
-        flops += 14.0 * D * S * S
-        units += 1
-    dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{units} whole (batch, head) units of the workload (S=8192, D=128, "
-                      f"non-causal), forward + backward in float64, {dt:.1f} s"}
+    with ProcessPoolExecutor(max_workers=cores, mp_context=mp.get_context("spawn"),
+                             initializer=_pin_blas) as ex:
+        while units < max_units and time.perf_counter() - t0 < target_seconds:
+            n = min(cores, max_units - units)
+            for f, _ in ex.map(_oracle_unit, [int(x) for x in rng.integers(1 << 30, size=n)]):
+                flops += f
+            units += n
+        wall = time.perf_counter() - t0
+        fut = ex.submit(_oracle_long_rows)
+        pairs, lflops, lsec = fut.result()
+    full_flops = 14.0 * D * 1883782890 * 32   # long workload: 30.86 + 77.16 TFLOP
+    return {"value": flops / wall / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{units} whole (batch, head) units of B2 S8192 H32 D128 non-causal, "
+                      f"forward + backward in float64, one process per unit on {cores} cores "
+                      f"with one BLAS thread each, {wall:.1f} s wall",
+            "long_causal_rows": {
+                "sample": "B1 S61380 H32 D128 causal: the 64 query rows the GPU test samples, "
+                          "row forward and row dQ in float64, one core",
+                "seconds": round(lsec, 2), "pairs": pairs,
+                "TFLOP/s": round(lflops / lsec / 1e12, 6),
+                "extrapolated_full_problem_seconds": round(full_flops / (lflops / lsec), 0),
+                "extrapolation": "whole forward + backward (30.86 + 77.16 TFLOP) at the "
+                                 "sample's measured per-FLOP rate on one core; not measured"}}
 
 
 def device_info(dev):
@@ -139,6 +205,35 @@ def fp8_forward(api, workloads, dev, flops, steps, warmup):
             "dtype": "e4m3 in, fp32 accumulate, bf16 out"}
 
 
+def side_measurements(api, dev, q, k, v, do, steps, warmup):
+    """Outside the timed region: the eager-rescale forward (fwd_variant 1) against the
+    default lazy one, and the fused backward (bwd_variant 1), whose dQ-reduce pass is an
+    HBM-bound conversion of the fp32 accumulator."""
+    import torch
+
+    res = {}
+    for name, fv in (("lazy", 0), ("eager", 1)):
+        for _ in range(warmup):
+            api.exattn_fwd(q, k, v, variant=fv)
+        torch.cuda.synchronize()
+        api.timing_read()
+        for _ in range(steps):
+            api.exattn_fwd(q, k, v, variant=fv)
+        torch.cuda.synchronize()
+        t, c = api.timing_read()["exattn_fwd_kernel"]
+        res[name] = t / c
+    out, lse = api.exattn_fwd(q, k, v)
+    for _ in range(2):
+        api.exattn_bwd(q, k, v, out, do, lse, variant=1)
+    torch.cuda.synchronize()
+    api.timing_read()
+    for _ in range(3):
+        api.exattn_bwd(q, k, v, out, do, lse, variant=1)
+    torch.cuda.synchronize()
+    kern = api.timing_read()
+    return res, {n: ms / c for n, (ms, c) in kern.items()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +246,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
+
+    # the CPU baseline runs first, before this process touches the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     import torch
 
@@ -214,13 +312,22 @@ def main():
     alg = per_kernel[dominant][0]
     achieved = alg / (kavg[dominant] * 1e-3) / 1e12
     traffic = measured_traffic(dominant)
+    api.timing_enable(True)
+    fwd_var, fused = side_measurements(api, dev, q, k, v, do, min(args.steps, 10), args.warmup)
+    api.timing_enable(False)
     side = {}
-    for name, nbytes in (("exattn_bwd_delta_kernel", 2 * 2 * B * S * H * D + 4 * B * H * S * 3),
-                         ("exattn_bwd_dq_reduce_kernel", 4 * B * S * H * D + 2 * B * S * H * D)):
-        if name in kavg:
-            gbs = nbytes / (kavg[name] * 1e-3) / 1e9
-            side[name] = {"ms": round(kavg[name], 4), "bytes": nbytes, "GB/s": round(gbs, 1),
+    for name, nbytes, src in (
+            ("exattn_bwd_delta_kernel", 2 * 2 * B * S * H * D + 4 * B * H * S * 3, kavg),
+            ("exattn_bwd_dq_reduce_kernel", 4 * B * S * H * D + 2 * B * S * H * D, fused)):
+        if name in src:
+            gbs = nbytes / (src[name] * 1e-3) / 1e9
+            side[name] = {"ms": round(src[name], 4), "bytes": nbytes, "GB/s": round(gbs, 1),
                           "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 3)}
+    side["exattn_bwd_dq_reduce_kernel"]["measured_in"] = (
+        "backward variant 1 (fused kernel with fp32 dQ atomics), outside the timed region")
+    lazy_eager = {"lazy_ms": round(fwd_var["lazy"], 4), "eager_ms": round(fwd_var["eager"], 4),
+                  "eager_over_lazy": round(fwd_var["eager"] / fwd_var["lazy"], 4),
+                  "fused_backward_kernel_ms": round(fused.get("exattn_bwd_fused_kernel", float("nan")), 4)}
 
     rec = {
         "metric": METRIC,
@@ -248,15 +355,19 @@ def main():
         "kernels_avg_ms": {n: round(t, 4) for n, t in kavg.items()},
         "kernels": kernels,
         "side_passes": side,
+        "forward_rescale": lazy_eager,
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "traffic_note": ("estimate: rocprofv3 FETCH_SIZE and WRITE_SIZE per launch, "
+                                      "each scaled by the same counter's reading on a plain copy "
+                                      "of known size; null once the kernel sources change"),
                      "algorithmic_flops_per_launch": alg},
     }
     if not args.no_fp8:
         rec["fp8_forward"] = fp8_forward(api, workloads, dev, fwd_flops, args.steps, args.warmup)
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline()
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)
 
 

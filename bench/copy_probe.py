@@ -2,7 +2,7 @@
 (FETCH_SIZE, WRITE_SIZE) that rocprofv3 reports for the attention kernels: the counters
 read for this copy, divided by the bytes it must move, give the scale factor.
 
-    python -m exact_attention_40_amd.copy_probe [MiB]
+    python bench/copy_probe.py [MiB]
 """
 
 import sys

@@ -7,7 +7,7 @@ Normalisation (MI355X: 8 XCDs, 256 CUs, 4 SIMDs per CU):
 - SQ_LDS_IDX_ACTIVE is summed over the CUs: LDS active = it / CUs per cycle;
 - SQ_INSTS_LDS_LOAD_BANDWIDTH counts 64-byte units loaded from LDS.
 
-    python -m exact_attention_40_amd.counter_summary PROF_DIR OUT.md [CUS]
+    python bench/counter_summary.py PROF_DIR OUT.md [CUS]
 """
 
 import collections
@@ -16,7 +16,7 @@ import glob
 import os
 import sys
 
-from .traffic import KERNELS, matches
+from traffic import KERNELS, matches
 
 PEAK_BF16_PER_CU_CLK = 4096.0   # dense bf16 FLOP per CU per clock
 
@@ -59,7 +59,7 @@ def main():
         "# Clock, MFMA and LDS utilisation per kernel: fwd + bwd step, B=2 S=8192 H=32 Hkv=32 D=128 (non-causal, bf16)",
         "",
         "Two `rocprofv3 --pmc` passes over `python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline`",
-        "(from the repository root; `exact_attention_40_amd/profile_bench.sh` runs them):",
+        "(from the repository root; `bench/profile_bench.sh` runs them):",
         "",
         "```",
         "rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES -d gpurun_out/prof/util -o bench -f csv -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",

@@ -1,7 +1,7 @@
 """Writes the kernel-duration and HBM-traffic summary for profiles/ from the output of
 profile_bench.sh (rocprofv3 kernel stats CSV and the per-kernel traffic JSON files).
 
-    python -m exact_attention_40_amd.profile_summary PROF_DIR OUT.md [TIMED_STEPS]
+    python bench/profile_summary.py PROF_DIR OUT.md [TIMED_STEPS]
 """
 
 import csv
@@ -10,7 +10,7 @@ import os
 import re
 import sys
 
-from .traffic import KERNELS, matches
+from traffic import KERNELS, matches
 
 MIN_BYTES = {  # algorithmic bytes per launch at B=2 S=8192 H=32 D=128 (bf16 tensors 134.2 MB, row vectors 2.1 MB)
     "exattn_fwd_kernel": ("q, k, v read 0.403 GB; out + lse written 0.136 GB", 0.4027, 0.1363),
@@ -55,7 +55,7 @@ def main():
         "per-dispatch trace); it is the figure to compare with bench.py's in-process HIP-event timing.",
         "\"avg\" includes the first (cold) calls.",
         "",
-        "Command (from the repository root; `exact_attention_40_amd/profile_bench.sh` runs all passes):",
+        "Command (from the repository root; `bench/profile_bench.sh` runs all passes):",
         "",
         "```",
         f"rocprofv3 --kernel-trace --stats -d gpurun_out/prof/trace -o bench -f csv -- python3 bench.py --steps {steps} --warmup 5 --no-cpu-baseline",
@@ -73,7 +73,7 @@ def main():
         "",
         "HBM bytes per launch: `rocprofv3 --pmc FETCH_SIZE` and, in a second run, `--pmc WRITE_SIZE` over",
         "`python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline`, each scaled by the same counter over",
-        "`python3 -m exact_attention_40_amd.copy_probe 512` (a copy of 512 MiB, three times).",
+        "`python3 bench/copy_probe.py 512` (a copy of 512 MiB, three times).",
     ]
     recs = {}
     for k in KERNELS:

@@ -6,7 +6,7 @@ WRITE_SIZE (KiB per dispatch) over the benchmark, and the same two counters over
 bytes moved; the benchmark's kernels are scaled by it and averaged per launch. The result
 is written as JSON next to the kernel source hash that bench.py checks.
 
-    python -m exact_attention_40_amd.traffic BENCH_FETCH.csv BENCH_WRITE.csv \
+    python bench/traffic.py BENCH_FETCH.csv BENCH_WRITE.csv \
         COPY_FETCH.csv COPY_WRITE.csv COPY_MIB OUT_DIR
 """
 

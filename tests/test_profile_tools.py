@@ -6,7 +6,10 @@ SQ_VALU_MFMA_BUSY_CYCLES summed over 4 SIMDs per CU, LDS activity and read bandw
 import csv
 import os
 
-from exact_attention_40_amd import counter_summary
+import sys
+
+sys.path.insert(0, os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "bench"))
+import counter_summary  # noqa: E402  (bench/counter_summary.py, a script beside bench.py)
 
 FIELDS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
           "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
