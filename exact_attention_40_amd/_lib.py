@@ -24,11 +24,12 @@ STATUS_NAMES = {
 ERR_HIP = 11
 
 DTYPE_BF16, DTYPE_FP16, DTYPE_FP8_E4M3 = 0, 1, 2
+NOALLOC_MAX_WORKSPACE = 32 << 20   # EXATTN_NOALLOC_MAX_WORKSPACE
 MASK_NONE, MASK_BOOL_U8, MASK_ADD_BF16 = 0, 1, 2
 
 EXPORTED = (
     "exattn_abi_version", "exattn_check", "exattn_fwd", "exattn_fwd_fp8", "exattn_bwd_workspace_size",
-    "exattn_bwd", "exattn_status_string", "exattn_last_error", "exattn_timing_enable",
+    "exattn_bwd", "exattn_bwd_noalloc", "exattn_status_string", "exattn_last_error", "exattn_timing_enable",
     "exattn_timing_read",
 )
 
@@ -78,6 +79,8 @@ def load():
         lib.exattn_bwd.restype = ctypes.c_int
         lib.exattn_bwd.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                    ctypes.c_size_t, _vp]
+        lib.exattn_bwd_noalloc.restype = ctypes.c_int
+        lib.exattn_bwd_noalloc.argtypes = [P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         lib.exattn_status_string.restype = ctypes.c_char_p
         lib.exattn_status_string.argtypes = [ctypes.c_int]
         lib.exattn_last_error.restype = ctypes.c_char_p

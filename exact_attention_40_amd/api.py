@@ -19,7 +19,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["exattn_fwd", "exattn_fwd_fp8", "exattn_bwd", "exattn_check", "attn_fwd", "attn_bwd", "attention",
+__all__ = ["exattn_fwd", "exattn_fwd_fp8", "exattn_bwd", "exattn_bwd_noalloc", "exattn_check", "attn_fwd", "attn_bwd", "attention",
            "AttnFunction", "timing_enable", "timing_read", "workspace_size"]
 
 
@@ -373,6 +373,46 @@ def exattn_bwd(q, k, v, out, dout, lse, *, causal=False, scale=None, mask=None,
     if st != _lib.OK:
         _fail(lib, st)
     return dq, dk, dv
+
+
+def exattn_bwd_noalloc(q, k, v, out, dout, lse, dq, dk, dv, *, causal=False, scale=None,
+                       mask=None, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
+                       max_seqlen_k=None, variant=0) -> None:
+    """Backward into caller-provided dq, dk, dv through exattn_bwd_noalloc, whose workspace
+    is a library-owned device array (include/exattn.h): the C call allocates nothing. The
+    tensors must already be in an accepted layout (head_dim contiguous, strides multiples of
+    8 elements, 16-byte aligned; dq/dk/dv contiguous), since a copy here would allocate;
+    a bool mask or host cu_seqlens still cost a conversion, so pass a uint8 mask and device
+    offsets with max_seqlen to keep the whole call allocation-free."""
+    lib = _lib.load()
+    spec = _Spec(q, k, v, causal, scale, mask, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                 max_seqlen_k, bwd_variant=variant)
+    for name, t, shape in (("out", out, spec.q_shape), ("dout", dout, spec.q_shape),
+                           ("dq", dq, spec.q_shape), ("dk", dk, tuple(k.shape)),
+                           ("dv", dv, tuple(v.shape))):
+        if not isinstance(t, torch.Tensor) or tuple(t.shape) != shape or t.dtype != spec.dtype:
+            raise ValueError(f"{name} must be a {spec.dtype} tensor of shape {shape}")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q is on {q.device}")
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if _norm(t) is not t:
+            raise ValueError(f"{name} is not in an accepted layout; a copy would allocate")
+    if (not isinstance(lse, torch.Tensor) or tuple(lse.shape) != spec.lse_shape
+            or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {spec.lse_shape}")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device)
+        with torch.cuda.stream(stream):
+            side = spec.prepare_side_inputs(q.device)
+            p = spec.problem(q, k, v, side, out=out, dout=dout)
+            st = lib.exattn_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                        _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                        ctypes.c_void_p(stream.cuda_stream))
+    if st != _lib.OK:
+        _fail(lib, st)
 
 
 attn_fwd = exattn_fwd

@@ -94,6 +94,11 @@ hipError_t timed(KernelId id, hipStream_t s, F&& f) {
   return e;
 }
 
+template <class F>
+hipError_t timed_if(bool timing, KernelId id, hipStream_t s, F&& f) {
+  return timing ? timed(id, s, f) : f();
+}
+
 // ---- validation --------------------------------------------------------------------------
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -417,13 +422,23 @@ size_t exattn_bwd_workspace_size(const exattn_problem* p) {
   return ws_layout(p).total;
 }
 
-exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, const void* v,
-                         const void* out, const void* dout, const float* lse, void* dq,
-                         void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                         void* stream) {
-  g_err[0] = 0;
-  exattn_status st = validate(p, true);
-  if (st != EXATTN_OK) return st;
+}  // extern "C"
+
+namespace exattn {
+namespace {
+
+// Workspace of the allocation-free backward: one array per GPU, resolved per device.
+constexpr size_t kScratchBytes = EXATTN_NOALLOC_MAX_WORKSPACE;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // device address of `scratch` per device id
+
+// The backward after validation: checks pointers and the workspace, then enqueues.
+// `timing` = false skips the timing events (their creation may allocate).
+exattn_status bwd_run(const exattn_problem* p, const void* q, const void* k, const void* v,
+                      const void* out, const void* dout, const float* lse, void* dq, void* dk,
+                      void* dv, void* workspace, size_t workspace_bytes, void* stream,
+                      bool timing) {
   const Geometry g = geometry(p);
   const bool anyq = g.rows_q > 0;
   const bool anyk = g.rows_k > 0;
@@ -496,16 +511,16 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
   if (!anyq) {
     // no query rows: every key receives zero gradient
     const int64_t bytes = g.rows_k * p->heads_kv * D * 2;
-    e = timed(KernelId::Zero, s, [&] { return launch_zero16(dk, bytes, s); });
-    if (e == hipSuccess) e = timed(KernelId::Zero, s, [&] { return launch_zero16(dv, bytes, s); });
+    e = timed_if(timing, KernelId::Zero, s, [&] { return launch_zero16(dk, bytes, s); });
+    if (e == hipSuccess) e = timed_if(timing, KernelId::Zero, s, [&] { return launch_zero16(dv, bytes, s); });
     if (e != hipSuccess) return hip_fail(e, "zero dk/dv");
     return EXATTN_OK;
   }
   if (order) {
-    e = timed(KernelId::UnitOrder, s, [&] { return launch_unit_order(a, order, s); });
+    e = timed_if(timing, KernelId::UnitOrder, s, [&] { return launch_unit_order(a, order, s); });
     if (e != hipSuccess) return hip_fail(e, "unit order launch");
   }
-  e = timed(KernelId::Delta, s, [&] { return launch_delta(a, D, p->dtype, g.varlen, s); });
+  e = timed_if(timing, KernelId::Delta, s, [&] { return launch_delta(a, D, p->dtype, g.varlen, s); });
   if (e != hipSuccess) return hip_fail(e, "delta kernel launch");
   const bool causal = p->causal != 0;
   if (a.num_k_blocks > 0) {
@@ -517,22 +532,70 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
     if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
   }
   if (fused) {
-    e = timed(KernelId::DqReduce, s, [&] { return launch_dq_reduce(a, D, s); });
+    e = timed_if(timing, KernelId::DqReduce, s, [&] { return launch_dq_reduce(a, D, s); });
     if (e != hipSuccess) return hip_fail(e, "dq reduce launch");
   } else {
-    e = timed(KernelId::BwdDq, s, [&] { return launch_bwd_dq(a, D, p->dtype, causal, p->mask_kind, g.varlen, s); });
+    e = timed_if(timing, KernelId::BwdDq, s, [&] { return launch_bwd_dq(a, D, p->dtype, causal, p->mask_kind, g.varlen, s); });
     if (e != hipSuccess) return hip_fail(e, "dq kernel launch");
     if (g.varlen) {
-      e = timed(KernelId::QTail, s, [&] { return launch_q_tail(a, D, s); });
+      e = timed_if(timing, KernelId::QTail, s, [&] { return launch_q_tail(a, D, s); });
       if (e != hipSuccess) return hip_fail(e, "q tail launch");
     }
   }
   if (g.varlen && anyk) {
-    e = timed(KernelId::KvTail, s, [&] { return launch_kv_tail(a, D, s); });
+    e = timed_if(timing, KernelId::KvTail, s, [&] { return launch_kv_tail(a, D, s); });
     if (e != hipSuccess) return hip_fail(e, "kv tail launch");
   }
   return EXATTN_OK;
 }
+
+}  // namespace
+}  // namespace exattn
+
+extern "C" {
+
+exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, const void* v,
+                         const void* out, const void* dout, const float* lse, void* dq,
+                         void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  g_err[0] = 0;
+  exattn_status st = validate(p, true);
+  if (st != EXATTN_OK) return st;
+  return bwd_run(p, q, k, v, out, dout, lse, dq, dk, dv, workspace, workspace_bytes, stream, true);
+}
+
+exattn_status exattn_bwd_noalloc(const exattn_problem* p, const void* q, const void* k,
+                                 const void* v, const void* out, const void* dout,
+                                 const float* lse, void* dq, void* dk, void* dv, void* stream) {
+  g_err[0] = 0;
+  exattn_status st = validate(p, true);
+  if (st != EXATTN_OK) return st;
+  const size_t need = ws_layout(p).total;
+  if (need > kScratchBytes)
+    return fail(EXATTN_ERR_WORKSPACE,
+                "this backward needs %zu bytes of workspace; exattn_bwd_noalloc holds at most %zu "
+                "(EXATTN_NOALLOC_MAX_WORKSPACE): use exattn_bwd with a caller workspace",
+                need, kScratchBytes);
+  // The array's device address, resolved once per device with that device current (each
+  // GPU holds its own copy of `scratch`; in host code the name is only a stand-in).
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+    if (!g_scratch_ptr[dev]) {
+      void* ptr = nullptr;
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      g_scratch_ptr[dev] = ptr;
+    }
+    ws = g_scratch_ptr[dev];
+  }
+  return bwd_run(p, q, k, v, out, dout, lse, dq, dk, dv, ws, kScratchBytes, stream, false);
+}
+
 
 exattn_status exattn_timing_enable(int enable) {
   std::lock_guard<std::mutex> lk(g_tmu);

@@ -241,6 +241,24 @@ exattn_status exattn_bwd(const exattn_problem* p, const void* q, const void* k, 
                          void* dk, void* dv, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/*
+ * Backward without any allocation, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * arguments and results as exattn_bwd, except that the workspace is a library-owned
+ * device array of EXATTN_NOALLOC_MAX_WORKSPACE bytes per GPU (resolved on the first call
+ * on each device, held until the process ends). The caller still passes every input and
+ * output. Problems whose exattn_bwd_workspace_size exceeds that maximum are rejected with
+ * EXATTN_ERR_WORKSPACE before anything is enqueued. Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (concurrent streams or threads) race on it
+ * and must not be issued; consecutive calls on one stream are safe (each call rewrites
+ * what it reads). The kernel timing of exattn_timing_enable does not cover this call.
+ * The current device must be the stream's device.
+ */
+#define EXATTN_NOALLOC_MAX_WORKSPACE ((size_t)32 << 20)
+exattn_status exattn_bwd_noalloc(const exattn_problem* p, const void* q, const void* k,
+                                 const void* v, const void* out, const void* dout,
+                                 const float* lse, void* dq, void* dk, void* dv, void* stream);
+
 /* Static description of a status code. Rejections are reported as statuses instead of
  * being run or silently accepted (cudnn-frontend PR #429, "Validate the input contract":
  * an unsupported input fails loudly with a message). */

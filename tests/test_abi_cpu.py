@@ -245,3 +245,19 @@ def test_host_cu_seqlens_checks():
                             ([0, 3, 10], 10, 6)):
         with pytest.raises(ValueError):
             api._host_cu_longest(c, total, "cu_seqlens_q", given)
+
+
+def test_noalloc_rejects_oversize_before_any_device_call(lib):
+    """The allocation-free backward holds at most EXATTN_NOALLOC_MAX_WORKSPACE bytes of
+    workspace; a larger problem is rejected before any HIP call (so this runs without a
+    GPU), and invalid problems are rejected as by exattn_bwd."""
+    D, H = 128, 32
+    p = _problem(batch=64, seqlen_q=8192, seqlen_k=8192, heads_q=H, heads_kv=H,
+                 q_stride=(8192 * H * D, H * D, D), k_stride=(8192 * H * D, H * D, D),
+                 v_stride=(8192 * H * D, H * D, D), o_stride=(8192 * H * D, H * D, D),
+                 do_stride=(8192 * H * D, H * D, D))
+    assert lib.exattn_bwd_workspace_size(ctypes.byref(p)) > _lib.NOALLOC_MAX_WORKSPACE
+    assert lib.exattn_bwd_noalloc(ctypes.byref(p), *([16] * 9), None) == 9
+    assert b"exattn_bwd_noalloc holds at most" in lib.exattn_last_error()
+    assert lib.exattn_bwd_noalloc(ctypes.byref(_problem(head_dim=96)), *([16] * 9), None) == 3
+    assert lib.exattn_bwd_noalloc(None, *([16] * 9), None) == 1
