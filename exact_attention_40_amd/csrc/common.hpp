@@ -54,6 +54,21 @@ struct Ty<f16> {
 
 __device__ __forceinline__ int acc_row(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
 
+// acc + the two 16-bit values packed in `pair` (a dot product with (1, 1): v_dot2c_f32_bf16 or
+// _f16), summing exponentials in the rounded form the P.V product consumes them.
+template <class E>
+__device__ __forceinline__ float add_pair(uint32_t pair, float acc);
+template <>
+__device__ __forceinline__ float add_pair<__bf16>(uint32_t pair, float acc) {
+  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2, pair), v2{(__bf16)1.f, (__bf16)1.f}, acc, false);
+}
+template <>
+__device__ __forceinline__ float add_pair<_Float16>(uint32_t pair, float acc) {
+  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(v2, pair), v2{(_Float16)1.f, (_Float16)1.f}, acc, false);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // An additive mask value in log2 units, bias * log2(e), rounded once. The product must not
@@ -245,6 +260,22 @@ __device__ __forceinline__ void copy_tile_async(unsigned char* dst, u32x4 rs, in
     const int row = pos / CPR, pc = pos % CPR;
     const int col = (pc ^ swz_f<D>(row)) * 8;
     copy16_to_lds(rs, (uint32_t)((row * stride + col) * 2), lds_addr(dst + p0 * 16));
+  }
+}
+// The same with `dst` given as an LDS byte address (wave-uniform), so no pointer conversion
+// happens per copy.
+template <int D, int R, int NW>
+__device__ __forceinline__ void copy_tile_async(uint32_t dst, u32x4 rs, int stride,
+                                                int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int ITER = R * CPR / 64 / NW;
+#pragma unroll
+  for (int i = 0; i < ITER; ++i) {
+    const int p0 = (i * NW + wave) * 64;
+    const int pos = p0 + lane;
+    const int row = pos / CPR, pc = pos % CPR;
+    const int col = (pc ^ swz_f<D>(row)) * 8;
+    copy16_to_lds(rs, (uint32_t)((row * stride + col) * 2), sgpr(dst + (uint32_t)p0 * 16u));
   }
 }
 

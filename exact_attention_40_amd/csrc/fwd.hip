@@ -74,6 +74,7 @@ fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform across the wave
   const int half = lane >> 5, l32 = lane & 31;
+  const uint32_t lds0 = lds_addr(smem);                        // LDS byte address of smem
 
   // Dense: consecutive blocks are the query tiles of one (unit, head), which share K/V in
   // one XCD's L2. Packed: query-tile index outermost, highest first, so that the longest
@@ -175,14 +176,14 @@ fwd_kernel(FwdArgs a) {
   auto load_k = [&](int t, int buf) {
     const int kb0 = t * T::BN;
     const int rows = min(T::BN, Sk - kb0);
-    copy_tile_async<D, T::BN, NW>(smem + buf * T::TBYTES,
+    copy_tile_async<D, T::BN, NW>(lds0 + buf * T::TBYTES,
                                   copy_rsrc(K + (int64_t)kb0 * a.k_ss, (uint32_t)((rows - 1) * a.k_ss + D) * 2u),
                                   (int)a.k_ss, wave, lane);
   };
   auto load_v = [&](int t, int buf) {
     const int kb0 = t * T::BN;
     const int rows = min(T::BN, Sk - kb0);
-    copy_tile_async<D, T::BN, NW>(smem + V_OFF + buf * T::TBYTES,
+    copy_tile_async<D, T::BN, NW>(lds0 + V_OFF + buf * T::TBYTES,
                                   copy_rsrc(V + (int64_t)kb0 * a.v_ss, (uint32_t)((rows - 1) * a.v_ss + D) * 2u),
                                   (int)a.v_ss, wave, lane);
   };
@@ -352,15 +353,9 @@ fwd_kernel(FwdArgs a) {
           pe = vis ? fast_exp2(fmaf(cur[eq][cb][r], c2, b2 - m_use[eq])) : 0.f;
         }
         cur[eq][cb][r] = pe;
-        rs[eq][r & 3] += pe;
-        asm volatile("" : "+v"(rs[eq][r & 3]));   // pin this step's exponential and sum here
+        asm volatile("" : "+v"(cur[eq][cb][r]));   // pin this step's exponential here
       }
       __builtin_amdgcn_sched_barrier(0x0004);
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      asm volatile("" : "+v"(rs[qb][0]), "+v"(rs[qb][1]), "+v"(rs[qb][2]), "+v"(rs[qb][3]));
-      l_run[qb] += (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
     }
     float mx[QB];
 #pragma unroll
@@ -371,9 +366,16 @@ fwd_kernel(FwdArgs a) {
       V8 pf[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
+      {
         pf[qb] = cvt8<V8>(cur[qb][kb][hs + 0], cur[qb][kb][hs + 1], cur[qb][kb][hs + 2],
                       cur[qb][kb][hs + 3], cur[qb][kb][hs + 4], cur[qb][kb][hs + 5],
                       cur[qb][kb][hs + 6], cur[qb][kb][hs + 7]);
+        // the row sum adds the exponentials as the P.V product sees them (rounded to the
+        // input format), two per instruction, so the output's weights sum to exactly 1
+        const u32x4 pw = __builtin_bit_cast(u32x4, pf[qb]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rs[qb][j] = add_pair<E>(pw[j], rs[qb][j]);
+      }
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) {
 #pragma unroll
@@ -409,6 +411,7 @@ fwd_kernel(FwdArgs a) {
     for (int qb = 0; qb < QB; ++qb) {
       asm volatile("" : "+v"(mx[qb]));   // keep the max chain inside the stream
       mt[qb] = MN ? pair_max32(mx[qb]) : pair_max32(mx[qb]) * c2;
+      l_run[qb] += (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
     }
   };
 
