@@ -1,6 +1,11 @@
-"""Plain device-to-device copy of a known size, used to calibrate the HBM byte counters
+"""Plain device-to-device copies of a known size, used to calibrate the HBM byte counters
 (FETCH_SIZE, WRITE_SIZE) that rocprofv3 reports for the attention kernels: the counters
-read for this copy, divided by the bytes it must move, give the scale factor.
+read for a copy, divided by the bytes it must move, give the scale factor.
+
+Two copies run, three times each: the runtime's own buffer copy (`copy_`), and an
+elementwise kernel (`x + 0` into `y`) whose lanes load and store 16 contiguous bytes each,
+the access width of the attention kernels' tile loads. The elementwise copy calibrates;
+the buffer copy checks that the factor does not depend on the copying kernel.
 
     python bench/copy_probe.py [MiB]
 """
@@ -20,7 +25,12 @@ def main():
         y.copy_(x)
     torch.cuda.synchronize()
     assert torch.equal(x[-4:], y[-4:])
-    print(f"copied {mib} MiB three times", flush=True)
+    y.zero_()
+    for _ in range(3):
+        torch.add(x, 0.0, out=y)
+    torch.cuda.synchronize()
+    assert torch.equal(x[-4:], y[-4:])
+    print(f"copied {mib} MiB three times by each of two kernels", flush=True)
 
 
 if __name__ == "__main__":

@@ -1,8 +1,8 @@
 #!/bin/bash
-# rocprofv3 passes over bench.py (kernel trace + stats, FETCH_SIZE, WRITE_SIZE, then clock /
-# MFMA and LDS utilisation counters) and over copy_probe (FETCH_SIZE and WRITE_SIZE) for the
-# HBM-traffic calibration. Writes raw output, the per-kernel traffic JSON and the two
-# summaries under gpurun_out/prof.
+# rocprofv3 passes over bench.py (kernel trace + stats, FETCH_SIZE, WRITE_SIZE, clock / MFMA
+# and LDS utilisation counters, instruction mix) and over copy_probe (FETCH_SIZE and
+# WRITE_SIZE) for the HBM-traffic calibration. Writes raw output, the per-kernel traffic JSON
+# and the two summaries under gpurun_out/prof.
 set -o pipefail
 export TMPDIR=/tmp
 R=${GRAFT_REPO_ROOT:-$(cd "$(dirname "$0")/.." && pwd)}
@@ -16,7 +16,8 @@ echo "copy fetch" && timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d $O/cfetch
 echo "copy write" && timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d $O/cwrite -o copy -f csv -- python3 bench/copy_probe.py 512 > $O/cwrite.log 2>&1 || exit 1
 echo "util" && timeout -s KILL 120 rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES -d $O/util -o bench -f csv -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline > $O/util.log 2>&1 || exit 1
 echo "lds" && timeout -s KILL 120 rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS_LOAD_BANDWIDTH SQ_LDS_BANK_CONFLICT -d $O/lds -o bench -f csv -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline > $O/lds.log 2>&1 || exit 1
-python3 bench/traffic.py $(ls $O/fetch/*counter_collection.csv) $(ls $O/write/*counter_collection.csv) $(ls $O/cfetch/*counter_collection.csv) $(ls $O/cwrite/*counter_collection.csv) 512 $O
+echo "mix" && timeout -s KILL 120 rocprofv3 --pmc SQ_WAVE_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_SCA SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_MFMA -d $O/mix -o bench -f csv -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline > $O/mix.log 2>&1 || exit 1
+python3 bench/traffic.py $(ls $O/fetch/*counter_collection.csv) $(ls $O/write/*counter_collection.csv) $(ls $O/cfetch/*counter_collection.csv) $(ls $O/cwrite/*counter_collection.csv) 512 $O 3
 python3 bench/profile_summary.py $O $O/exattn_b2_s8192_h32_d128_kernel_stats.md 20
 python3 bench/counter_summary.py $O $O/exattn_b2_s8192_h32_d128_counters.md
 # the per-kernel JSON files and the summary land in gpurun_out/prof; copy them into profiles/

@@ -73,7 +73,8 @@ def main():
         "",
         "HBM bytes per launch: `rocprofv3 --pmc FETCH_SIZE` and, in a second run, `--pmc WRITE_SIZE` over",
         "`python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline`, each scaled by the same counter over",
-        "`python3 bench/copy_probe.py 512` (a copy of 512 MiB, three times).",
+        "`python3 bench/copy_probe.py 512` (512 MiB copied three times by each of two kernels), and",
+        "averaged over each kernel's first 3 dispatches (the benchmark's warm-up and timed steps).",
     ]
     recs = {}
     for k in KERNELS:
@@ -83,7 +84,10 @@ def main():
     if recs:
         cal = next(iter(recs.values()))["copy_calibration"]
         lines += [
-            f"FETCH_SIZE reads 1/{cal['fetch_factor']:.3f} of the copied bytes, WRITE_SIZE 1/{cal['write_factor']:.3f}.",
+            f"For the elementwise copy, whose lanes move 16 contiguous bytes like the attention kernels'",
+            f"tile loads, FETCH_SIZE reads 1/{cal['fetch_factor']:.3f} of the copied bytes and WRITE_SIZE",
+            f"1/{cal['write_factor']:.3f}; these factors scale the table. The runtime's buffer copy reads",
+            f"1/{cal.get('runtime_copy_fetch_factor', float('nan')):.3f} and 1/{cal.get('runtime_copy_write_factor', float('nan')):.3f}.",
             "The per-kernel JSON files next to this one hold the numbers with the kernel source hash",
             f"bench.py checks ({next(iter(recs.values()))['source_hash']}).",
             "",

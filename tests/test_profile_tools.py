@@ -10,6 +10,7 @@ import sys
 
 sys.path.insert(0, os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "bench"))
 import counter_summary  # noqa: E402  (bench/counter_summary.py, a script beside bench.py)
+import traffic  # noqa: E402,F401  (bench/traffic.py)
 
 FIELDS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
           "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
@@ -61,3 +62,49 @@ def test_counter_summary_normalisation(tmp_path, monkeypatch):
     assert cells[4] == f"{cus * 4096 * 1.8e9 / 1e12:.0f}"   # peak at the held clock
     assert cells[5] == "37.5%"                 # LDS active
     assert cells[6] == "96.0"                  # LDS read bytes per clock per CU
+
+
+def _write_counts(path, rows, counter):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for d, (name, kib) in enumerate(rows, 1):
+            row = {k: 0 for k in FIELDS}
+            row.update(Dispatch_Id=d, Kernel_Name=name, Counter_Name=counter, Counter_Value=kib)
+            w.writerow(row)
+
+
+def test_traffic_scaling_and_dispatch_window(tmp_path, monkeypatch):
+    """Known answers for the traffic step: the elementwise copy sets the scale, the runtime
+    copy is only recorded, small dispatches do not dilute either factor, and only each
+    kernel's first dispatches are averaged."""
+    import json
+    import traffic
+
+    mib = 64
+    copy_kib = mib * 1024
+    ew = "void at::native::vectorized_elementwise_kernel<4, at::native::CUDAFunctorOnSelf_add<float>>"
+    fill = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float>>"
+    rt = "__amd_rocclr_copyBuffer"
+    # read counter: 1/2 of the bytes for the elementwise copy, 3/8 for the runtime copy; a
+    # tiny runtime copy (the probe's result check) and a fill are left out of the factors
+    _write_counts(tmp_path / "cf.csv", [(rt, copy_kib * 3 / 8)] * 3 + [(rt, 1.5), (fill, 10)]
+                  + [(ew, copy_kib / 2)] * 3, "FETCH_SIZE")
+    _write_counts(tmp_path / "cw.csv", [(rt, copy_kib)] * 3 + [(rt, 0.03), (fill, copy_kib)]
+                  + [(ew, copy_kib)] * 3, "WRITE_SIZE")
+    # delta kernel: three main-loop dispatches, then two with extra writes that must be left out
+    _write_counts(tmp_path / "bf.csv", [(KNAME.replace("13bwd_dq_kernel", "12delta_kernel"), 1000)] * 5,
+                  "FETCH_SIZE")
+    _write_counts(tmp_path / "bw.csv", [(KNAME.replace("13bwd_dq_kernel", "12delta_kernel"), w)
+                                        for w in (10, 10, 10, 5000, 5000)], "WRITE_SIZE")
+    monkeypatch.setattr("sys.argv", ["x", str(tmp_path / "bf.csv"), str(tmp_path / "bw.csv"),
+                                     str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"), str(mib),
+                                     str(tmp_path), "3"])
+    traffic.main()
+    rec = json.load(open(tmp_path / "exattn_bwd_delta_kernel_b2_s8192_h32_d128_pmc.json"))
+    assert rec["copy_calibration"]["fetch_factor"] == 2.0
+    assert abs(rec["copy_calibration"]["runtime_copy_fetch_factor"] - 8 / 3) < 1e-12
+    assert rec["copy_calibration"]["runtime_copy_write_factor"] == 1.0
+    assert rec["fetch_bytes_per_launch"] == 1000 * 1024 * 2.0
+    assert rec["write_bytes_per_launch"] == 10 * 1024
