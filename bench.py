@@ -234,6 +234,30 @@ def side_measurements(api, dev, q, k, v, do, steps, warmup):
     return res, {n: ms / c for n, (ms, c) in kern.items()}
 
 
+def stored_ds_steps(api, q, k, v, do, steps, warmup):
+    """Outside the timed region: whole steps (forward + backward variant 3, whose dK/dV
+    kernel stores dS and whose dQ pass is dS K from it) timed like the benchmark's own
+    steps, with the per-kernel averages."""
+    import torch
+
+    def step():
+        out, lse = api.exattn_fwd(q, k, v)
+        api.exattn_bwd(q, k, v, out, do, lse, variant=3)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    api.timing_read()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    kern = api.timing_read()
+    return t0.elapsed_time(t1) / steps, {n: ms / c for n, (ms, c) in kern.items()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -314,6 +338,7 @@ def main():
     traffic = measured_traffic(dominant)
     api.timing_enable(True)
     fwd_var, fused = side_measurements(api, dev, q, k, v, do, min(args.steps, 10), args.warmup)
+    sds_ms, sds = stored_ds_steps(api, q, k, v, do, min(args.steps, 10), args.warmup)
     api.timing_enable(False)
     side = {}
     for name, nbytes, src in (
@@ -325,6 +350,19 @@ def main():
                           "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 3)}
     side["exattn_bwd_dq_reduce_kernel"]["measured_in"] = (
         "backward variant 1 (fused kernel with fp32 dQ atomics), outside the timed region")
+    ds_bytes = B * H * (S // 64) * (S // 128) * 16384
+    sds_bwd = sum(t for n, t in sds.items() if n != "exattn_fwd_kernel")
+    stored = {"step_ms": round(sds_ms, 4), "TFLOP/s": round((fwd_flops + bwd_flops) / sds_ms / 1e9, 1),
+              "fwd_kernel_ms": round(sds.get("exattn_fwd_kernel", float("nan")), 4),
+              "bwd_ms": round(sds_bwd, 4),
+              "kernels_avg_ms": {n: round(t, 4) for n, t in sds.items()},
+              "ds_bytes": ds_bytes,
+              "note": ("backward variant 3 (dS stored by the dK/dV kernel, dQ = dS K from it), "
+                       "whole steps outside the timed region; not the default")}
+    if "exattn_bwd_dq_ds_kernel" in sds:
+        gbs = (ds_bytes + 2 * B * S * H * D) / (sds["exattn_bwd_dq_ds_kernel"] * 1e-3) / 1e9
+        stored["dq_ds_GB/s"] = round(gbs, 1)
+        stored["dq_ds_frac_of_hbm_peak"] = round(gbs / PEAK_HBM_GBS, 3)
     lazy_eager = {"lazy_ms": round(fwd_var["lazy"], 4), "eager_ms": round(fwd_var["eager"], 4),
                   "eager_over_lazy": round(fwd_var["eager"] / fwd_var["lazy"], 4),
                   "fused_backward_kernel_ms": round(fused.get("exattn_bwd_fused_kernel", float("nan")), 4)}
@@ -356,6 +394,7 @@ def main():
         "kernels": kernels,
         "side_passes": side,
         "forward_rescale": lazy_eager,
+        "stored_ds_backward": stored,
         "roofline": {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,

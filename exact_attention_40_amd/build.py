@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libexattn.so")
-SOURCES = ["fwd.hip", "fwd_fp8.hip", "bwd.hip", "bwd_kv.hip", "api.cpp"]
+SOURCES = ["fwd.hip", "fwd_fp8.hip", "bwd.hip", "bwd_kv.hip", "bwd_dq_ds.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -29,6 +29,7 @@ const char* kernel_name(KernelId id) {
     case KernelId::Zero: return "exattn_zero_kernel";
     case KernelId::FwdFp8: return "exattn_fwd_fp8_kernel";
     case KernelId::UnitOrder: return "exattn_bwd_unit_order_kernel";
+    case KernelId::BwdDqDs: return "exattn_bwd_dq_ds_kernel";
     default: return "unknown";
   }
 }
@@ -152,8 +153,8 @@ exattn_status validate(const exattn_problem* p, bool bwd, bool fp8 = false) {
     return fail(EXATTN_ERR_SHAPE, "the fp8 forward has one tiling: fwd_variant and bwd_variant must be 0");
   if (p->fwd_variant < 0 || p->fwd_variant > 2)
     return fail(EXATTN_ERR_SHAPE, "unknown fwd_variant %d (0, 1 or 2)", p->fwd_variant);
-  if (p->bwd_variant < 0 || p->bwd_variant > 2)
-    return fail(EXATTN_ERR_SHAPE, "unknown bwd_variant %d (0, 1 or 2)", p->bwd_variant);
+  if (p->bwd_variant < 0 || p->bwd_variant > 3)
+    return fail(EXATTN_ERR_SHAPE, "unknown bwd_variant %d (0, 1, 2 or 3)", p->bwd_variant);
   if ((int64_t)p->heads_q * p->head_dim >= kMaxTokenStride16 ||
       (int64_t)p->heads_kv * p->head_dim >= kMaxTokenStride16)
     return fail(EXATTN_ERR_SHAPE, "heads * head_dim must be below 2^23 elements");
@@ -226,8 +227,16 @@ bool fused_backward(const exattn_problem* p) {
   return p->bwd_variant == 1 && p->dtype == EXATTN_DTYPE_BF16;
 }
 
+// Variant 3 stores dS for dense layouts whose dS fits kMaxStoredDs bytes; other problems
+// run variant 0.
+constexpr size_t kMaxStoredDs = (size_t)64 << 30;
+bool stored_ds(const exattn_problem* p) {
+  return p->bwd_variant == 3 && p->cu_seqlens_q == nullptr &&
+         stored_ds_bytes(p->batch, p->heads_q, p->seqlen_q, p->seqlen_k) <= kMaxStoredDs;
+}
+
 struct WsLayout {
-  size_t lse2, delta, order, dq_acc, total;
+  size_t lse2, delta, order, dq_acc, ds, total;
 };
 
 // Packed layouts with at most kMaxOrderedUnits sequences get a ranking of the sequences
@@ -244,7 +253,8 @@ WsLayout ws_layout(const exattn_problem* p) {
   w.delta = w.lse2 + align256(nq * sizeof(float));
   w.order = w.delta + align256(nq * sizeof(float));
   w.dq_acc = w.order + (ordered_units(p) ? align256((size_t)p->num_seqs * sizeof(int32_t)) : 0);
-  w.total = w.dq_acc + (fused_backward(p) ? align256(nq * p->head_dim * sizeof(float)) : 0);
+  w.ds = w.dq_acc + (fused_backward(p) ? align256(nq * p->head_dim * sizeof(float)) : 0);
+  w.total = w.ds + (stored_ds(p) ? stored_ds_bytes(p->batch, p->heads_q, p->seqlen_q, p->seqlen_k) : 0);
   return w;
 }
 
@@ -503,6 +513,9 @@ exattn_status bwd_run(const exattn_problem* p, const void* q, const void* k, con
   a.scale = p->scale;
   a.scale_log2 = (float)((double)p->scale * 1.4426950408889634);
   a.rotate = fused ? 1 : 0;
+  const bool sds = stored_ds(p);
+  a.ds = sds ? ws + w.ds : nullptr;
+  a.ds_nqt = (p->seqlen_q + 63) / 64;
   if ((((int64_t)a.num_units + 7) / 8 * 8) * a.Hkv * a.num_k_blocks > INT32_MAX ||
       (int64_t)a.num_units * H * a.num_q_blocks > INT32_MAX)
     return fail(EXATTN_ERR_SHAPE, "too many blocks");
@@ -526,7 +539,7 @@ exattn_status bwd_run(const exattn_problem* p, const void* q, const void* k, con
   if (a.num_k_blocks > 0) {
     const bool pipelined = !fused && p->bwd_variant != 2;
     e = timed(fused ? KernelId::BwdFused : KernelId::BwdDkDv, s, [&] {
-      return pipelined ? launch_bwd_kv(a, D, p->dtype, causal, p->mask_kind, g.varlen, s)
+      return pipelined ? launch_bwd_kv(a, D, p->dtype, causal, p->mask_kind, g.varlen, sds, s)
                        : launch_bwd(a, D, p->dtype, causal, p->mask_kind, g.varlen, fused, s);
     });
     if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
@@ -534,6 +547,9 @@ exattn_status bwd_run(const exattn_problem* p, const void* q, const void* k, con
   if (fused) {
     e = timed_if(timing, KernelId::DqReduce, s, [&] { return launch_dq_reduce(a, D, s); });
     if (e != hipSuccess) return hip_fail(e, "dq reduce launch");
+  } else if (sds) {
+    e = timed_if(timing, KernelId::BwdDqDs, s, [&] { return launch_bwd_dq_ds(a, D, p->dtype, causal, s); });
+    if (e != hipSuccess) return hip_fail(e, "dq kernel launch");
   } else {
     e = timed_if(timing, KernelId::BwdDq, s, [&] { return launch_bwd_dq(a, D, p->dtype, causal, p->mask_kind, g.varlen, s); });
     if (e != hipSuccess) return hip_fail(e, "dq kernel launch");

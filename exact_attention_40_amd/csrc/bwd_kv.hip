@@ -18,6 +18,12 @@
 // Delta rows are copied global -> LDS with asynchronous copies; each phase ends with one
 // wait that leaves only the copies of tile t + 2 in flight, then the barrier.
 //
+// Stored dS (SDS, dense layouts): wave B also writes each dS fragment it forms, rounded to
+// the input format as for its own dK product, so that a separate pass can form dQ = dS K
+// without recomputing S and dP. Chunk (unit, head, 64-row query tile, key block, key group,
+// 16-row slab) is 1 KB: 32 bytes per key, the lanes' 16-byte halves side by side, key index
+// XOR 4 on odd slabs (the reader's transposed LDS reads then touch every bank once).
+//
 // Sources: dv = P^T dO and dk = dS^T q (flash-dmattn PR #122 "Fix NaN/Inf values in dV
 // gradients during backward pass", section "Solution", item 2); P = exp(s - lse) from the
 // stored LSE, with partial key and query tiles masked in the kernel (OpenWAM PR #64,
@@ -51,8 +57,9 @@ struct KvTile {
   static_assert(SMEM <= 160 * 1024, "fits the 160 KB of LDS");
 };
 
-template <class E, int D, bool CAUSAL, int MASK, bool VARLEN>
+template <class E, int D, bool CAUSAL, int MASK, bool VARLEN, bool SDS>
 __global__ void __launch_bounds__(512) bwd_kv_kernel(BwdArgs a) {
+  static_assert(!(SDS && VARLEN), "stored dS is laid out for dense problems");
   using T = KvTile<D>;
   using V8 = typename Ty<E>::v8;
   using V4 = typename Ty<E>::v4;
@@ -217,6 +224,7 @@ __global__ void __launch_bounds__(512) bwd_kv_kernel(BwdArgs a) {
   };
   constexpr int NCOPY = 2 * (T::BM * T::CPR / 64 / T::NW);   // tile copies per wave
 
+  TilePos prv = {h_beg, qstart};   // tile t - 1 (wave B's dS and dK)
   TilePos cur = {h_beg, qstart};   // tile t (wave A)
   TilePos nxt = cur;               // tile t + 1
   advance(nxt);
@@ -350,9 +358,15 @@ __global__ void __launch_bounds__(512) bwd_kv_kernel(BwdArgs a) {
   };
 
   // ---- wave B, previous tile: dS = P * (dP - Delta); dK += dS^T Q ----------------------------
-  auto dk_step = [&](int qslot, int pslot, int sslot) {
+  auto dk_step = [&](int qslot, int pslot, int sslot, const TilePos& tp) {
     const int tro = qslot * T::QBYTES;
     const unsigned char* pr = pp + pslot * T::P_BYTES;
+    E* dsw = nullptr;   // this wave's four dS chunks of the tile (SDS)
+    if constexpr (SDS) {
+      const int64_t chunk = ((((int64_t)unit * a.H + tp.head) * a.ds_nqt + tp.q0 / T::BM) *
+                                 a.num_k_blocks + kbi) * 16 + kg * 4;
+      dsw = reinterpret_cast<E*>(a.ds) + chunk * 512 + half * 8;
+    }
     V4 tb[2][T::DB][2];
     auto tload = [&](int kk, int slot) {
 #pragma unroll
@@ -376,6 +390,8 @@ __global__ void __launch_bounds__(512) bwd_kv_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e) d[4 * h + e] = pv[e] * (sp[qb][hs + 4 * h + e] - dd[e]);
       }
       const V8 sa = cvt8<V8>(d[0], d[1], d[2], d[3], d[4], d[5], d[6], d[7]);
+      if constexpr (SDS)   // streaming store: dS is read back once, by the dQ pass
+        __builtin_nontemporal_store(sa, reinterpret_cast<V8*>(dsw + kk * 512 + (l32 ^ (4 * (kk & 1))) * 16));
       if (kk + 1 < NKK) tload(kk + 1, (kk + 1) & 1);
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) {
@@ -424,6 +440,7 @@ __global__ void __launch_bounds__(512) bwd_kv_kernel(BwdArgs a) {
       // tile t + 2 may still be in flight
       if (t + 2 < n_iter) sync_copies<NCOPY>();
       else sync_copies<0>();
+      prv = cur;
       cur = nxt;
       nxt = nx2;
       advance(nx2);
@@ -446,7 +463,7 @@ __global__ void __launch_bounds__(512) bwd_kv_kernel(BwdArgs a) {
     });
   } else {
     run_phases([&](int t, int, int s2, int p3, int, int q4p, int d3, auto copy_next) {
-      if (t >= 1) dk_step(q4p, s2 ^ 1, p3);
+      if (t >= 1) dk_step(q4p, s2 ^ 1, p3, prv);
       copy_next();
       if (t < n_iter) dp_step(d3);
     });
@@ -463,7 +480,7 @@ __global__ void __launch_bounds__(512) bwd_kv_kernel(BwdArgs a) {
                         krows - kg * 32, lane);
 }
 
-template <class E, int D>
+template <class E, int D, bool SDS>
 static hipError_t launch_bwd_kv_d(const BwdArgs& a, bool causal, int mask, bool varlen, hipStream_t s) {
   // with a sequence ranking (packed): 8 XCDs x ceil(units / 8) slots of whole sequences
   const int64_t units = (varlen && a.unit_order) ? 8 * (((int64_t)a.num_units + 7) / 8) : a.num_units;
@@ -473,7 +490,7 @@ static hipError_t launch_bwd_kv_d(const BwdArgs& a, bool causal, int mask, bool 
   constexpr int smem = KvTile<D>::SMEM;
 #define EXATTN_BWD_KV(C, M, V)                                                                 \
   do {                                                                                         \
-    auto kfn = bwd_kv_kernel<E, D, C, M, V>;                                                   \
+    auto kfn = bwd_kv_kernel<E, D, C, M, V, SDS && !V>;                                        \
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                     \
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);      \
     if (e != hipSuccess) return e;                                                             \
@@ -495,14 +512,21 @@ static hipError_t launch_bwd_kv_d(const BwdArgs& a, bool causal, int mask, bool 
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_kv(const BwdArgs& a, int head_dim, int dtype, bool causal, int mask,
-                         bool varlen, hipStream_t s) {
+template <bool SDS>
+static hipError_t launch_bwd_kv_s(const BwdArgs& a, int head_dim, int dtype, bool causal, int mask,
+                                  bool varlen, hipStream_t s) {
   if (dtype == kDtypeF16) {
-    if (head_dim == 64) return launch_bwd_kv_d<f16, 64>(a, causal, mask, varlen, s);
-    return launch_bwd_kv_d<f16, 128>(a, causal, mask, varlen, s);
+    if (head_dim == 64) return launch_bwd_kv_d<f16, 64, SDS>(a, causal, mask, varlen, s);
+    return launch_bwd_kv_d<f16, 128, SDS>(a, causal, mask, varlen, s);
   }
-  if (head_dim == 64) return launch_bwd_kv_d<bf16, 64>(a, causal, mask, varlen, s);
-  return launch_bwd_kv_d<bf16, 128>(a, causal, mask, varlen, s);
+  if (head_dim == 64) return launch_bwd_kv_d<bf16, 64, SDS>(a, causal, mask, varlen, s);
+  return launch_bwd_kv_d<bf16, 128, SDS>(a, causal, mask, varlen, s);
+}
+
+hipError_t launch_bwd_kv(const BwdArgs& a, int head_dim, int dtype, bool causal, int mask,
+                         bool varlen, bool store_ds, hipStream_t s) {
+  if (store_ds && !varlen) return launch_bwd_kv_s<true>(a, head_dim, dtype, causal, mask, false, s);
+  return launch_bwd_kv_s<false>(a, head_dim, dtype, causal, mask, varlen, s);
 }
 
 }  // namespace exattn

@@ -235,6 +235,11 @@ __device__ __forceinline__ void copy16_to_lds(u32x4 rsrc, uint32_t voff, uint32_
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                : : "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
 }
+// The same as a streaming (non-temporal) load, for data read exactly once.
+__device__ __forceinline__ void copy16_to_lds_nt(u32x4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+               : : "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
+}
 __device__ __forceinline__ void copy4_to_lds(u32x4 rsrc, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                : : "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");

@@ -44,6 +44,7 @@ struct BwdArgs {
   float* lse2;       // fp32, lse layout: lse * log2(e), +inf for empty rows
   float* delta;      // fp32, lse layout: rowsum(dout * out)
   const int32_t* unit_order;  // packed: sequences by query length, longest first (NULL = in order)
+  void* ds;          // stored dS chunks (backward variant 3, dense only), else NULL
   int64_t q_sb, q_ss, q_sh;
   int64_t k_sb, k_ss, k_sh;
   int64_t v_sb, v_ss, v_sh;
@@ -63,13 +64,14 @@ struct BwdArgs {
   int rows_q;        // rows of q per head in total: B*Sq (dense) or total_q (packed)
   int rows_k;
   int rotate;        // query-tile order: 0 = in order, 1 = spread by key block, 2 = offset kbi % 8
+  int ds_nqt;        // stored dS: 64-row query tiles per (unit, head), ceil(Sq / 64)
   float scale;
   float scale_log2;
 };
 
 enum class KernelId : int {
   Fwd = 0, FwdTail, Delta, BwdDkDv, BwdDq, BwdFused, DqReduce, KvTail, QTail, Zero, FwdFp8,
-  UnitOrder, Count
+  UnitOrder, BwdDqDs, Count
 };
 
 const char* kernel_name(KernelId id);
@@ -81,8 +83,13 @@ hipError_t launch_fwd_tail(const FwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_delta(const BwdArgs& a, int head_dim, int dtype, bool varlen, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, int dtype, bool causal, int mask_mode,
                       bool varlen, bool fused_dq, hipStream_t s);
+// Pipelined dK/dV kernel (default); with `store_ds` (dense only) it also writes dS to a.ds.
 hipError_t launch_bwd_kv(const BwdArgs& a, int head_dim, int dtype, bool causal, int mask_mode,
-                         bool varlen, hipStream_t s);  // pipelined dK/dV kernel (default)
+                         bool varlen, bool store_ds, hipStream_t s);
+// dQ = dS K from the stored dS (dense only).
+hipError_t launch_bwd_dq_ds(const BwdArgs& a, int head_dim, int dtype, bool causal, hipStream_t s);
+// Bytes of the stored dS for a dense problem: B * H * ceil(Sq / 64) * ceil(Sk / 128) * 16 KiB.
+size_t stored_ds_bytes(int64_t batch, int64_t heads, int64_t sq, int64_t sk);
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int dtype, bool causal, int mask_mode,
                          bool varlen, hipStream_t s);
 hipError_t launch_q_tail(const BwdArgs& a, int head_dim, hipStream_t s);

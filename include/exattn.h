@@ -170,7 +170,12 @@ typedef struct exattn_problem {
  *     bitwise reproducible; 1: one fused kernel that adds dQ partial products into an fp32
  *     workspace accumulator with atomics, then a conversion pass (bf16 only, larger
  *     workspace; fp16 problems run variant 0); 2: as 0 with a dK/dV kernel whose two waves
- *     per key group work on the same query tile, two barriers per tile.
+ *     per key group work on the same query tile, two barriers per tile; 3: as 0, but the
+ *     dK/dV kernel also stores every dS tile it forms (rounded to the input format, as for
+ *     its dK product) in the workspace, and dQ = dS K is formed from it without recomputing
+ *     S and dP; bitwise reproducible. Dense layouts whose dS takes at most 64 GiB
+ *     (batch * heads_q * ceil(seqlen_q / 64) * ceil(seqlen_k / 128) * 16 KiB); other
+ *     problems run variant 0.
  * Other values are rejected with EXATTN_ERR_SHAPE.
  */
 

@@ -124,7 +124,7 @@ def test_check_accepts_valid_problem(lib):
     (dict(heads_q=65536, heads_kv=1), 4),      # heads * head_dim reaches 2^23
     (dict(fwd_variant=3), 4),                  # per-call tiling selectors
     (dict(fwd_variant=-1), 4),
-    (dict(bwd_variant=3), 4),
+    (dict(bwd_variant=4), 4),
     (dict(reserved=1), 4),
 ])
 def test_check_rejects(lib, kw, status):
@@ -227,6 +227,15 @@ def test_variant_is_per_call(lib):
     assert ws[2] == ws[0]
     # fp16 runs the split backward for every variant
     assert lib.exattn_bwd_workspace_size(ctypes.byref(_problem(dtype=1, bwd_variant=1))) == ws[0]
+    # the stored-dS variant adds B * H * ceil(Sq / 64) * ceil(Sk / 128) chunks of 16 KiB
+    ws3 = lib.exattn_bwd_workspace_size(ctypes.byref(_problem(bwd_variant=3)))
+    assert ws3 == ws[0] + 2 * 4 * 2 * 1 * 16384
+    # ... for dense layouts only: packed ones run variant 0
+    packed = dict(batch=1, seqlen_q=100, seqlen_k=100, num_seqs=2, max_seqlen_q=60,
+                  max_seqlen_k=60, cu_seqlens_q=4096, cu_seqlens_k=4096,
+                  k_stride=(0, 2 * 128, 128), v_stride=(0, 2 * 128, 128))
+    assert (lib.exattn_bwd_workspace_size(ctypes.byref(_problem(bwd_variant=3, **packed))) ==
+            lib.exattn_bwd_workspace_size(ctypes.byref(_problem(bwd_variant=0, **packed))))
     for v in (0, 1, 2):
         assert lib.exattn_check(ctypes.byref(_problem(fwd_variant=v))) == 0
     # the fp8 forward has one tiling
