@@ -22,33 +22,28 @@ import glob
 import os
 import sys
 
-from traffic import KERNELS, matches
+from traffic import KERNELS, kernel_key
 
 PEAK_BF16_PER_CU_CLK = 4096.0   # dense bf16 FLOP per CU per clock
 
 
-def short(name):
-    for k, t in KERNELS.items():
-        if matches(name, t):
-            return k
-    return None
-
-
-def load(pass_dir, last=2):
-    """{kernel: {counter: [(value, seconds)]}} over each kernel's last `last` dispatches."""
+def load(pass_dir, skip=1, take=2):
+    """{kernel: {counter: [(value, seconds)]}} over each kernel's dispatches skip .. skip +
+    take - 1 in issue order: with --warmup 1 --steps 2, the benchmark's two timed steps
+    (its side measurements, which run other variants, come after them)."""
     files = glob.glob(os.path.join(pass_dir, "*counter_collection.csv"))
     if not files:
         raise SystemExit(f"no counter CSV under {pass_dir}")
     rows = collections.defaultdict(lambda: collections.defaultdict(list))
     for r in csv.DictReader(open(files[0])):
-        k = short(r["Kernel_Name"])
+        k = kernel_key(r["Kernel_Name"])
         if k is None:
             continue
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
         rows[k][r["Counter_Name"]].append((int(r["Dispatch_Id"]), float(r["Counter_Value"]), dur))
     out = {}
     for k, d in rows.items():
-        out[k] = {c: [(v, t) for _, v, t in sorted(x)[-last:]] for c, x in d.items()}
+        out[k] = {c: [(v, t) for _, v, t in sorted(x)[skip:skip + take]] for c, x in d.items()}
     return out
 
 
@@ -74,7 +69,9 @@ def main():
         "rocprofv3 --pmc SQ_WAVE_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_SCA SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_MFMA -d gpurun_out/prof/mix -o bench -f csv -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
         "```",
         "",
-        f"Averages over each kernel's last two dispatches; {cus} CUs, 8 XCDs. \"held clock\" is",
+        f"Averages over each kernel's two timed dispatches (after one warm-up call); {cus} CUs, 8",
+        "XCDs. The stored-dS kernels (backward variant 3) come from the benchmark's side",
+        "measurement, also its first two calls after one warm-up. \"held clock\" is",
         "GRBM_GUI_ACTIVE per XCD over the dispatch duration. \"MFMA busy\" is",
         "SQ_VALU_MFMA_BUSY_CYCLES per SIMD over those cycles; for the matrix kernels it equals",
         "the executed MFMA work (32 busy cycles per 32x32x16 MFMA). \"of held-clock peak\" is the",

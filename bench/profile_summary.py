@@ -1,7 +1,7 @@
 """Writes the kernel-duration and HBM-traffic summary for profiles/ from the output of
 profile_bench.sh (rocprofv3 kernel stats CSV and the per-kernel traffic JSON files).
 
-    python bench/profile_summary.py PROF_DIR OUT.md [TIMED_STEPS]
+    python bench/profile_summary.py PROF_DIR OUT.md [TIMED_STEPS [WARMUP]]
 """
 
 import csv
@@ -10,7 +10,7 @@ import os
 import re
 import sys
 
-from traffic import KERNELS, matches
+from traffic import KERNELS, kernel_key
 
 MIN_BYTES = {  # algorithmic bytes per launch at B=2 S=8192 H=32 D=128 (bf16 tensors 134.2 MB, row vectors 2.1 MB)
     "exattn_fwd_kernel": ("q, k, v read 0.403 GB; out + lse written 0.136 GB", 0.4027, 0.1363),
@@ -18,47 +18,50 @@ MIN_BYTES = {  # algorithmic bytes per launch at B=2 S=8192 H=32 D=128 (bf16 ten
     "exattn_bwd_dq_kernel": ("q, k, v, dout 0.537 GB + stats 0.004 GB read; dq 0.134 GB written", 0.5411, 0.1342),
     "exattn_bwd_delta_kernel": ("out, dout 0.268 GB + lse read; delta, lse2 0.004 GB written", 0.2705, 0.0042),
     "exattn_fwd_fp8_kernel": ("e4m3 q, k, v read 0.201 GB; bf16 out + lse written 0.136 GB", 0.2013, 0.1363),
+    "exattn_bwd_dkdv_ds_kernel": ("as dK/dV; written: dk, dv 0.268 GB + dS 8.590 GB", 0.5411, 8.8584),
+    "exattn_bwd_dq_ds_kernel": ("dS 8.590 GB + k 0.134 GB read; dq 0.134 GB written", 8.7242, 0.1342),
 }
 
 
 def short(name):
-    for k, t in KERNELS.items():
-        if matches(name, t):
-            return k
-    return name
+    return kernel_key(name) or name
 
 
-def timed_averages(prof, steps):
-    """Average duration (ms) of each kernel over its last `steps` dispatches: the calls of
-    the benchmark's timed steps (the trace also holds the warm-up calls)."""
+def timed_averages(prof, steps, warmup):
+    """Average duration (ms) of each kernel instance over its dispatches warmup .. warmup +
+    steps - 1 in issue order: the benchmark's timed steps (the trace also holds the warm-up
+    calls and, after the timed steps, the side measurements of other variants)."""
     durs = {}
     for r in csv.DictReader(open(os.path.join(prof, "trace", "bench_kernel_trace.csv"))):
         durs.setdefault(r["Kernel_Name"], []).append(
             (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
     out = {}
     for name, d in durs.items():
-        last = [x for _, x in sorted(d)][-steps:]
-        out[name] = sum(last) / len(last) / 1e6
+        sel = [x for _, x in sorted(d)][warmup:warmup + steps]
+        if sel:
+            out[name] = sum(sel) / len(sel) / 1e6
     return out
 
 
 def main():
     prof, out = sys.argv[1:3]
     steps = int(sys.argv[3]) if len(sys.argv) > 3 else 20
+    warmup = int(sys.argv[4]) if len(sys.argv) > 4 else 5
     rows = list(csv.DictReader(open(os.path.join(prof, "trace", "bench_kernel_stats.csv"))))
-    timed = timed_averages(prof, steps)
+    timed = timed_averages(prof, steps, warmup)
     lines = [
         "# Kernel durations and HBM traffic: fwd + bwd step, B=2 S=8192 H=32 Hkv=32 D=128 (non-causal, bf16)",
         "",
         "Kernel trace (rocprofv3 `--kernel-trace --stats`) over the benchmark's warm-up and timed steps.",
-        f"\"timed avg\" is the mean over each kernel's last {steps} dispatches (the timed steps, from the",
-        "per-dispatch trace); it is the figure to compare with bench.py's in-process HIP-event timing.",
+        f"\"timed avg\" is the mean over each kernel instance's dispatches {warmup} .. {warmup + steps - 1} (the timed",
+        "steps, from the per-dispatch trace; the side measurements of other variants come after",
+        "them); it is the figure to compare with bench.py's in-process HIP-event timing.",
         "\"avg\" includes the first (cold) calls.",
         "",
         "Command (from the repository root; `bench/profile_bench.sh` runs all passes):",
         "",
         "```",
-        f"rocprofv3 --kernel-trace --stats -d gpurun_out/prof/trace -o bench -f csv -- python3 bench.py --steps {steps} --warmup 5 --no-cpu-baseline",
+        f"rocprofv3 --kernel-trace --stats -d gpurun_out/prof/trace -o bench -f csv -- python3 bench.py --steps {steps} --warmup {warmup} --no-cpu-baseline",
         "```",
         "",
         "| kernel | instance | calls | timed avg ms | avg ms | min ms | max ms | share |",

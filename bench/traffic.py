@@ -24,7 +24,9 @@ import sys
 KERNELS = {  # library timing name -> kernel template name (rocprofv3 may or may not demangle)
     "exattn_fwd_kernel": "fwd_kernel",
     "exattn_bwd_dkdv_kernel": "bwd_kv_kernel",
+    "exattn_bwd_dkdv_ds_kernel": "bwd_kv_kernel",      # the instance that also stores dS
     "exattn_bwd_dq_kernel": "bwd_dq_kernel",
+    "exattn_bwd_dq_ds_kernel": "bwd_dq_ds_kernel",
     "exattn_bwd_delta_kernel": "delta_kernel",
     "exattn_fwd_fp8_kernel": "fwd_fp8_kernel",
 }
@@ -35,6 +37,21 @@ def matches(kernel_name, template):
     return (f"exattn::{template}<" in kernel_name
             or f"N6exattn{len(template)}{template}I" in kernel_name
             or f"ZN6exattn{len(template)}{template}I" in kernel_name)
+
+
+def stores_ds(kernel_name):
+    """True for the dK/dV kernel instance whose last template argument (store dS) is true."""
+    return kernel_name.endswith("Lb1EEEvNS_7BwdArgsE") or kernel_name.endswith(", true>(exattn::BwdArgs)")
+
+
+def kernel_key(kernel_name):
+    """The library timing name of a kernel instance name, or None for other kernels."""
+    for k, t in KERNELS.items():
+        if matches(kernel_name, t):
+            if t == "bwd_kv_kernel":
+                return "exattn_bwd_dkdv_ds_kernel" if stores_ds(kernel_name) else "exattn_bwd_dkdv_kernel"
+            return k
+    return None
 
 
 def source_hash():
@@ -88,9 +105,9 @@ def main():
     wscale_rt = copy_factor(cw, "WRITE_SIZE", copy_bytes, "runtime")
     fetch, write = per_kernel(bf, "FETCH_SIZE", first), per_kernel(bw, "WRITE_SIZE", first)
     shash = source_hash()
-    for name, sub in KERNELS.items():
-        fk = [v for k, v in fetch.items() if matches(k, sub)]
-        wk = [v for k, v in write.items() if matches(k, sub)]
+    for name in KERNELS:
+        fk = [v for k, v in fetch.items() if kernel_key(k) == name]
+        wk = [v for k, v in write.items() if kernel_key(k) == name]
         if not fk or not wk:
             continue
         rec = {

@@ -108,3 +108,20 @@ def test_traffic_scaling_and_dispatch_window(tmp_path, monkeypatch):
     assert rec["copy_calibration"]["runtime_copy_write_factor"] == 1.0
     assert rec["fetch_bytes_per_launch"] == 1000 * 1024 * 2.0
     assert rec["write_bytes_per_launch"] == 10 * 1024
+
+
+def test_kernel_key_separates_the_ds_storing_instance():
+    """The dK/dV kernel that also stores dS (last template argument true) gets its own
+    row, in mangled and demangled spellings; other instances keep theirs."""
+    import traffic
+
+    m = "_ZN6exattn13bwd_kv_kernelIDF16bLi128ELb0ELi0ELb0ELb{}EEEvNS_7BwdArgsE"
+    assert traffic.kernel_key(m.format(0)) == "exattn_bwd_dkdv_kernel"
+    assert traffic.kernel_key(m.format(1)) == "exattn_bwd_dkdv_ds_kernel"
+    d = "void exattn::bwd_kv_kernel<__bf16, 128, false, 0, false, {}>(exattn::BwdArgs)"
+    assert traffic.kernel_key(d.format("false")) == "exattn_bwd_dkdv_kernel"
+    assert traffic.kernel_key(d.format("true")) == "exattn_bwd_dkdv_ds_kernel"
+    assert traffic.kernel_key("_ZN6exattn16bwd_dq_ds_kernelIDF16bLi128ELb0EEEvNS_7BwdArgsE") == \
+        "exattn_bwd_dq_ds_kernel"
+    assert traffic.kernel_key(KNAME) == "exattn_bwd_dq_kernel"
+    assert traffic.kernel_key("__amd_rocclr_copyBuffer") is None
