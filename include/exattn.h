@@ -220,7 +220,9 @@ exattn_status exattn_fwd_fp8(const exattn_problem* p, const void* q, const void*
 
 /* Bytes of device workspace exattn_bwd needs for this problem (its bwd_variant included):
  * fp32 [lse * log2(e) | rowsum(dout * out)] per (row, head), an int32 ranking of the
- * packed sequences, and for bwd_variant 1 the fp32 dQ accumulator. The workspace is the
+ * packed sequences, for bwd_variant 1 the fp32 dQ accumulator, and for bwd_variant 3 the
+ * stored dS (B * heads_q * ceil(seqlen_q / 64) * ceil(seqlen_k / 128) * 16 KiB, 8.6 GB at
+ * B2 S8192 H32). The workspace is the
  * caller's memory, as every buffer is (NVIDIA cudnn-frontend PR #429, first commit
  * message: the caller owns the scratch the backward needs and its zero-fill is enqueued on
  * the launch stream). Returns 0 on invalid input. */

@@ -12,15 +12,17 @@ from gpu_util import gpu_inputs, say
 pytestmark = pytest.mark.gpu
 
 
-def _both(p):
+def _both(p, variant=0):
     q, k, v, do, kw = gpu_inputs(p)
+    kw["variant"] = variant
     if p.varlen:   # device offsets, so the binding converts nothing
         kw = dict(kw, cu_seqlens_q=p.cu_seqlens_q.cuda(), cu_seqlens_k=p.cu_seqlens_k.cuda(),
                   max_seqlen_q=int((p.cu_seqlens_q[1:] - p.cu_seqlens_q[:-1]).max()),
                   max_seqlen_k=int((p.cu_seqlens_k[1:] - p.cu_seqlens_k[:-1]).max()))
     if p.mask is not None and p.mask.dtype == torch.bool:
         kw["mask"] = kw["mask"].to(torch.uint8).bool()
-    out, lse = api.exattn_fwd(q, k, v, **kw)
+    fkw = {n: x for n, x in kw.items() if n != "variant"}
+    out, lse = api.exattn_fwd(q, k, v, **fkw)
     ref = api.exattn_bwd(q, k, v, out, do, lse, **kw)
     got = [torch.full_like(t, float("nan")) for t in ref]
     api.exattn_bwd_noalloc(q, k, v, out, do, lse, *got, **kw)
@@ -51,6 +53,20 @@ def test_noalloc_matches_bwd_on_consecutive_calls():
             assert torch.isfinite(b).all(), (name, n)
             assert torch.equal(a, b), (name, n, float((a.float() - b.float()).abs().max()))
         say(f"  noalloc == bwd: {name}")
+
+
+def test_noalloc_stored_ds_variant():
+    """Backward variant 3 keeps dS in the workspace: through the array too, when it fits
+    (16 MB here, then a smaller problem); bit for bit exattn_bwd's outputs."""
+    for name, make in (("dense B2 S1000 H4 Hkv2 D128 causal",
+                        lambda: workloads.dense(2, 1000, 1000, 4, 2, 128, seed=9011, causal=True)),
+                       ("dense B1 S300 H2 Hkv1 D64",
+                        lambda: workloads.dense(1, 300, 260, 2, 1, 64, seed=9012))):
+        ref, got = _both(make(), variant=3)
+        for n, a, b in zip(("dq", "dk", "dv"), ref, got):
+            assert torch.isfinite(b).all(), (name, n)
+            assert torch.equal(a, b), (name, n, float((a.float() - b.float()).abs().max()))
+        say(f"  noalloc == bwd, stored dS: {name}")
 
 
 def test_noalloc_rejects_problem_beyond_the_array():
