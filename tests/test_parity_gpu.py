@@ -369,19 +369,20 @@ def test_fully_masked_rows_and_uniform_scale():
     np.testing.assert_allclose(f64(g2["lse"]), math.log(90), rtol=1e-6)
 
 
-def test_empty_inputs():
+@pytest.mark.parametrize("bwd_variant", [0, 1, 2, 3])
+def test_empty_inputs(bwd_variant):
     q = torch.zeros(2, 0, 4, 128, dtype=torch.bfloat16, device="cuda")
     k = torch.randn(2, 50, 4, 128, device="cuda").bfloat16()
     out, lse = api.exattn_fwd(q, k, k)
     assert out.shape == (2, 0, 4, 128) and lse.shape == (2, 4, 0)
-    dq, dk, dv = api.exattn_bwd(q, k, k, out, q, lse)
+    dq, dk, dv = api.exattn_bwd(q, k, k, out, q, lse, variant=bwd_variant)
     torch.cuda.synchronize()
     assert torch.count_nonzero(dk) == 0 and torch.count_nonzero(dv) == 0
     # no keys: every row is empty
     q = torch.randn(1, 70, 2, 64, device="cuda").bfloat16()
     k0 = torch.zeros(1, 0, 2, 64, dtype=torch.bfloat16, device="cuda")
     out, lse = api.exattn_fwd(q, k0, k0)
-    dq, dk, dv = api.exattn_bwd(q, k0, k0, out, torch.randn_like(q), lse)
+    dq, dk, dv = api.exattn_bwd(q, k0, k0, out, torch.randn_like(q), lse, variant=bwd_variant)
     torch.cuda.synchronize()
     assert torch.count_nonzero(out) == 0 and torch.isneginf(lse).all()
     assert torch.count_nonzero(dq) == 0
