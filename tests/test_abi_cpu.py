@@ -236,6 +236,23 @@ def test_variant_is_per_call(lib):
                   k_stride=(0, 2 * 128, 128), v_stride=(0, 2 * 128, 128))
     assert (lib.exattn_bwd_workspace_size(ctypes.byref(_problem(bwd_variant=3, **packed))) ==
             lib.exattn_bwd_workspace_size(ctypes.byref(_problem(bwd_variant=0, **packed))))
+    # ... and only while dS takes at most 64 GiB: B1 S61380 H32 would need 236 GB
+    S, H, D = 61380, 32, 128
+    big = dict(batch=1, seqlen_q=S, seqlen_k=S, heads_q=H, heads_kv=H, causal=1,
+               q_stride=(S * H * D, H * D, D), k_stride=(S * H * D, H * D, D),
+               v_stride=(S * H * D, H * D, D), o_stride=(S * H * D, H * D, D),
+               do_stride=(S * H * D, H * D, D))
+    assert (lib.exattn_bwd_workspace_size(ctypes.byref(_problem(bwd_variant=3, **big))) ==
+            lib.exattn_bwd_workspace_size(ctypes.byref(_problem(bwd_variant=0, **big))))
+    # while B2 S8192 H32 stores its 8.6 GB
+    S = 8192
+    mid = dict(big, batch=2, seqlen_q=S, seqlen_k=S, causal=0,
+               q_stride=(S * H * D, H * D, D), k_stride=(S * H * D, H * D, D),
+               v_stride=(S * H * D, H * D, D), o_stride=(S * H * D, H * D, D),
+               do_stride=(S * H * D, H * D, D))
+    assert (lib.exattn_bwd_workspace_size(ctypes.byref(_problem(bwd_variant=3, **mid))) -
+            lib.exattn_bwd_workspace_size(ctypes.byref(_problem(bwd_variant=0, **mid)))) == \
+        2 * 32 * 128 * 64 * 16384
     for v in (0, 1, 2):
         assert lib.exattn_check(ctypes.byref(_problem(fwd_variant=v))) == 0
     # the fp8 forward has one tiling
