@@ -192,3 +192,42 @@ def test_nan_input_propagates_and_stays_local():
     lk[0, 1, 77] = False
     assert torch.equal(l1[lk], l0[lk])
     assert torch.isnan(dk1).all() and torch.isnan(dv1).all()
+
+
+@pytest.mark.parametrize("bwd_variant", [0, 3])
+def test_graph_capture_replays(bwd_variant):
+    """The calls enqueue only kernels (zero-fills included, no memset nodes), so a caller
+    may capture them in a HIP graph. Forward, backward and the allocation-free backward are
+    captured once and replayed three times, with eager work and a synchronisation between
+    the replays; every replay reproduces the eager results bit for bit."""
+    p = workloads.dense(2, 300, 260, 4, 2, 128, seed=7301, causal=True)
+    q, k, v, do, kw = gpu_inputs(p)
+    out, lse = api.exattn_fwd(q, k, v, **kw)
+    ref = (out, lse) + tuple(api.exattn_bwd(q, k, v, out, do, lse, variant=bwd_variant, **kw))
+    nq = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    api.exattn_bwd_noalloc(q, k, v, out, do, lse, *nq, variant=bwd_variant, **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(ref[2:], nq):
+        assert torch.equal(a, b)
+
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph):
+            g_out, g_lse = api.exattn_fwd(q, k, v, **kw)
+            g_grads = api.exattn_bwd(q, k, v, g_out, do, g_lse, variant=bwd_variant, **kw)
+            api.exattn_bwd_noalloc(q, k, v, g_out, do, g_lse, *nq, variant=bwd_variant, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    got = (g_out, g_lse) + tuple(g_grads)
+    for rep in range(3):
+        for t in got + tuple(nq):
+            t.fill_(float("nan"))          # eager work between the replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("out", "lse", "dq", "dk", "dv"), ref, got):
+            assert torch.equal(a, b), (rep, name)
+        for name, a, b in zip(("dq", "dk", "dv"), ref[2:], nq):
+            assert torch.equal(a, b), (rep, "noalloc " + name)
+    say(f"  graph replays match eager (backward variant {bwd_variant})")
