@@ -150,6 +150,7 @@ constexpr size_t bwd_smem_bytes() {
 
 template <class E, int D, bool CAUSAL, int MASK, bool VARLEN, bool DQ>
 __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
+  nan_passing_clamp();   // NaN passes the clamped exponential below (no NaN is cleaned)
   using T = BwdTile<D>;
   using V8 = typename Ty<E>::v8;
   using V4 = typename Ty<E>::v4;
@@ -380,7 +381,7 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rg + e;
           if constexpr (!EDGE) {
-            s[r] = fast_exp2(min0(fmaf(s[r], c2, -l2[e])));
+            s[r] = exp2_le1(fmaf(s[r], c2, -l2[e]));
           } else {
             // Branch-free visibility: mask reads use indices clamped into range.
             const int qi = qt0 + qb * 32 + 8 * rg + 4 * half + e;
@@ -397,7 +398,7 @@ __global__ void __launch_bounds__(512) bwd_kernel(BwdArgs a) {
                 b2 = vis ? bias_log2(bias) : 0.f;
               }
             }
-            const float e2 = fast_exp2(min0(fmaf(s[r], c2, b2 - l2[e])));
+            const float e2 = exp2_le1(fmaf(s[r], c2, b2 - l2[e]));
             s[r] = vis ? e2 : 0.f;
           }
         }
@@ -559,6 +560,7 @@ struct DqTile {
 
 template <class E, int D, bool CAUSAL, int MASK, bool VARLEN>
 __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
+  nan_passing_clamp();   // NaN passes the clamped exponential below (no NaN is cleaned)
   using T = DqTile<D>;
   using V8 = typename Ty<E>::v8;
   using V4 = typename Ty<E>::v4;
@@ -709,7 +711,7 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
     auto ds_elem = [&](int kb, int r) {
       float p;
       if constexpr (!MASKED) {
-        p = fast_exp2(min0(fmaf(s[kb][r], c2, -l2)));
+        p = exp2_le1(fmaf(s[kb][r], c2, -l2));
       } else {
         const int kj = kb0 + kb * 32 + acc_row(r, half);
         bool vis = (kj < Sk) && (qi < Sq);
@@ -725,7 +727,7 @@ __global__ void __launch_bounds__(512) bwd_dq_kernel(BwdArgs a) {
             b2 = vis ? bias_log2(bias) : 0.f;
           }
         }
-        const float e2 = fast_exp2(min0(fmaf(s[kb][r], c2, b2 - l2)));
+        const float e2 = exp2_le1(fmaf(s[kb][r], c2, b2 - l2));
         p = vis ? e2 : 0.f;
       }
       dp[kb][r] = p * (dp[kb][r] - dl);

@@ -59,6 +59,7 @@ struct KvTile {
 
 template <class E, int D, bool CAUSAL, int MASK, bool VARLEN, bool SDS>
 __global__ void __launch_bounds__(512) bwd_kv_kernel(BwdArgs a) {
+  nan_passing_clamp();   // NaN passes the clamped exponential below (no NaN is cleaned)
   static_assert(!(SDS && VARLEN), "stored dS is laid out for dense problems");
   using T = KvTile<D>;
   using V8 = typename Ty<E>::v8;
@@ -266,7 +267,7 @@ __global__ void __launch_bounds__(512) bwd_kv_kernel(BwdArgs a) {
       if ((r & 3) == 0) l2v = lds_at<f32x4>(st_rd, sslot * T::BM * 4 + (qb * 32 + 8 * (r >> 2)) * 4);
       const float lv = l2v[r & 3];
       if constexpr (MASK == kMaskNone) {
-        sp[qb][r] = fast_exp2(min0(fmaf(sp[qb][r], c2, -lv)));
+        sp[qb][r] = exp2_le1(fmaf(sp[qb][r], c2, -lv));
       } else {
         // Branch-free visibility: mask reads use indices clamped into range.
         const int qi = qt0 + qb * 32 + acc_row(r, half);
@@ -281,7 +282,7 @@ __global__ void __launch_bounds__(512) bwd_kv_kernel(BwdArgs a) {
           vis = vis && (bias != -INFINITY);
           b2 = vis ? bias_log2(bias) : 0.f;
         }
-        const float e2 = fast_exp2(min0(fmaf(sp[qb][r], c2, b2 - lv)));
+        const float e2 = exp2_le1(fmaf(sp[qb][r], c2, b2 - lv));
         sp[qb][r] = vis ? e2 : 0.f;
       }
     };

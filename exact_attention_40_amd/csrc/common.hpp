@@ -70,6 +70,21 @@ __device__ __forceinline__ float add_pair<_Float16>(uint32_t pair, float acc) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// exp2(min(x, 0)) in one instruction: exp2 is monotonic, so that is exp2(x) clamped to
+// [0, 1], which the output clamp of v_exp_f32 gives (+inf -> 1, -inf -> 0). The clamp maps
+// NaN to 0 unless the mode register's DX10_CLAMP bit is clear: kernels that use this call
+// nan_passing_clamp() first, so a NaN score or lse stays NaN (a plain min(x, 0) before the
+// exponential would turn it into exp2(0) = 1). No other instruction in those kernels
+// carries a clamp modifier.
+__device__ __forceinline__ float exp2_le1(float x) {
+  float r;
+  asm("v_exp_f32_e64 %0, %1 clamp" : "=v"(r) : "v"(x));
+  return r;
+}
+// Clear MODE.DX10_CLAMP (bit 8) for this wave: clamped float results keep NaN.
+__device__ __forceinline__ void nan_passing_clamp() {
+  asm volatile("s_setreg_imm32_b32 hwreg(HW_REG_MODE, 8, 1), 0");
+}
 
 // An additive mask value in log2 units, bias * log2(e), rounded once. The product must not
 // be contracted into a later add (hipcc fuses across statements by default): the row max
@@ -81,9 +96,6 @@ __device__ __forceinline__ float bias_log2(float bias) {
   return bias * kLog2e;
 }
 
-// min(x, 0) that keeps NaN (v_minimum3_f32): the backward's exponent clamp must not turn a
-// NaN score or lse into exp2(0) = 1.
-__device__ __forceinline__ float min0(float x) { return __builtin_elementwise_minimum(x, 0.f); }
 
 template <bool B>
 using bool_c = std::integral_constant<bool, B>;
