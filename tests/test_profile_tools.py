@@ -125,3 +125,22 @@ def test_kernel_key_separates_the_ds_storing_instance():
         "exattn_bwd_dq_ds_kernel"
     assert traffic.kernel_key(KNAME) == "exattn_bwd_dq_kernel"
     assert traffic.kernel_key("__amd_rocclr_copyBuffer") is None
+
+
+def test_bench_traffic_follows_the_source_hash(tmp_path, monkeypatch):
+    """bench.py reports roofline.traffic from a committed counter record only while the
+    record's kernel source hash is the sources' hash (the same hash the traffic step
+    writes); a stale or missing record gives null."""
+    import json
+    import bench
+
+    assert bench.kernel_source_hash() == traffic.source_hash()
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    name = "exattn_bwd_dkdv_kernel"
+    assert bench.measured_traffic(name) is None                       # no record
+    path = tmp_path / f"{name}_b2_s8192_h32_d128_pmc.json"
+    path.write_text(json.dumps({"source_hash": bench.kernel_source_hash(),
+                                "hbm_bytes_per_launch": 1234.5}))
+    assert bench.measured_traffic(name) == 1234.5                     # current record
+    path.write_text(json.dumps({"source_hash": "0" * 16, "hbm_bytes_per_launch": 1234.5}))
+    assert bench.measured_traffic(name) is None                       # stale record
